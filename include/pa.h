@@ -1,0 +1,183 @@
+/*
+ * pa.h -- C ABI of libpa, a paged-attention library for AMD MI355X (gfx950).
+ *
+ * The method: each sequence's K/V cache lives in fixed-size physical blocks
+ * drawn from one pre-allocated pool; a per-sequence block table maps logical
+ * block floor(pos / B) to a physical block id, and the token sits at offset
+ * pos mod B inside it.  Attention for a query is softmax(q K^T * scale) V
+ * over the sequence's keys, gathered through the table.  Passages defining
+ * it: "High-Throughput Local LLM Infrastructure: Architecting a Distributed
+ * Go API Gateway for vLLM & PagedAttention Clusters", section "1.2
+ * PagedAttention Mechanics & Virtual Page Tables" (pool, block table, index
+ * and offset equations, kernels taking the block table as a lookup
+ * argument); "03 -- PagedAttention & the vLLM V1 Architecture", section "The
+ * attention kernel side"; "Inside vLLM: Anatomy of a High-Throughput LLM
+ * Inference System (2025)", section "Physical Block Mapping and Kernel
+ * Invocation".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or retains memory, holds no mutable
+ *    global state and is re-entrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it and the call returns once it is enqueued, so
+ *    stream order gives slot mapping -> cache write -> attention.
+ *  - The return value is a pa_status, known synchronously.  Argument
+ *    checks (null pointers, sizes, head counts, dtype, workspace size) are
+ *    made before anything is enqueued.  A failed launch returns PA_ERR_HIP.
+ *  - Metadata that lives on the device (block tables, seq_lens, slots,
+ *    query_start_loc) cannot be checked without a copy.  Kernels stay
+ *    memory-safe on any values (indices are clamped or skipped), but
+ *    out-of-contract values give unspecified results.  With the environment
+ *    variable PA_CHECK=1 the library copies that metadata to the host,
+ *    validates it (ranges, seq_len >= 1, seq_len <= max_blocks_per_seq * B,
+ *    q_len <= seq_len, no duplicate slot), synchronises the stream and
+ *    returns PA_ERR_INDEX on a violation.
+ *
+ * Layouts (one attention layer; e = element size)
+ * -----------------------------------------------
+ *   k_cache       [num_blocks, H_kv, B, D]   token rows, head_dim contiguous
+ *   v_cache       [num_blocks, H_kv, D, B]   head_dim rows, B tokens contiguous
+ *   query, out    [T, H_q, D]                packed rows (T = tokens this step)
+ *   key, value    [T, H_kv, D]               this step's new K/V
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens      int32 [num_seqs]   tokens per sequence INCLUDING this step's
+ *   query_start_loc int32 [num_seqs + 1]; rows of sequence s are
+ *                 [qsl[s], qsl[s+1]), at positions seq_len - q_len .. seq_len-1
+ *   slot_mapping  int64 [T]; slot = block_id * B + offset; < 0 = skip
+ *  Query head h reads KV head h / (H_q / H_kv).  A query at position P sees
+ *  keys 0..P.  `out` has the dtype of `query`.
+ *
+ * Supported: dtype PA_F32 or PA_BF16; head_dim 64 or 128; block_size a
+ * power of two from 1 to 64; H_q % H_kv == 0 with 1 <= H_q / H_kv <= 16;
+ * kv_split_tokens 0 (auto) or a multiple of 64 with
+ * kv_split_tokens <= 64 * max(block_size, 8).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  PA_ERR_SHAPE = -2,       /* a size or count is out of range / inconsistent */
+  PA_ERR_DTYPE = -3,       /* unknown dtype                                  */
+  PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim, B, G)     */
+  PA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required        */
+  PA_ERR_INDEX = -6,       /* PA_CHECK=1 found bad device metadata           */
+  PA_ERR_HIP = -7          /* a HIP runtime call or a launch failed          */
+} pa_status;
+
+/* Human-readable name of a pa_status value (static string, never NULL). */
+const char* pa_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/*
+ * pa_compute_slot_mapping -- slot of every query token.
+ * Defined by the index and offset equations (logical block = floor(pos/B),
+ * offset = pos mod B) in "High-Throughput Local LLM Infrastructure ...",
+ * section "1.2 PagedAttention Mechanics & Virtual Page Tables".
+ *   slot_mapping[qsl[s] + j] = block_tables[s][pos / B] * B + pos % B,
+ *   pos = seq_lens[s] - q_len_s + j.
+ * query_start_loc may be NULL: one query token per sequence (decode), and
+ * then num_tokens must equal num_seqs.  Tokens whose position is negative or
+ * beyond the table get slot -1.
+ */
+int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs,
+                            int32_t num_tokens, int32_t block_size,
+                            void* stream);
+
+/*
+ * pa_reshape_and_cache -- write this step's K/V into their cache slots.
+ * The write of newly computed K/V into the physical blocks a sequence was
+ * assigned: "High-Throughput Local LLM Infrastructure ...", section "2.1
+ * PagedAttention Memory Allocation Life-Cycle", step 4.
+ *   k_cache[slot / B][h][slot % B][:] = key[t][h][:]
+ *   v_cache[slot / B][h][:][slot % B] = value[t][h][:]
+ * for every token t with 0 <= slot < num_blocks * B.  Values are copied bit
+ * for bit.  Two tokens with one slot race (forbidden; PA_CHECK reports it).
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                         void* v_cache, const int64_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * Workspace for pa_decode: split-K partial results (running max, sum and
+ * unnormalised output per query row and context split).  kv_split_tokens is
+ * the number of keys one split covers (0 = the library chooses); pass the
+ * same value to pa_decode.  Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_seq_len,
+                                 int32_t block_size, int32_t kv_split_tokens);
+
+/*
+ * pa_decode -- one query token per sequence against its paged K/V.
+ * Attention definition: "03 -- PagedAttention & the vLLM V1 Architecture",
+ * section "The attention kernel side"; gather: "Inside vLLM ...", section
+ * "Physical Block Mapping and Kernel Invocation".
+ *   out[s][h] = softmax_t(scale * query[s][h] . K_s[t][h/G]) . V_s[t][h/G],
+ *   t = 0 .. seq_lens[s]-1, K_s/V_s gathered through block_tables[s].
+ * max_seq_len must be >= every seq_len.  Long contexts are cut into splits
+ * of kv_split_tokens keys whose partial results are merged exactly
+ * (log-sum-exp) in a second pass.
+ */
+int pa_decode(void* out, const void* query, const void* k_cache,
+              const void* v_cache, const int32_t* block_tables,
+              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+              int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t num_blocks, float scale, int32_t dtype,
+              int32_t kv_split_tokens, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Workspace for pa_chunked_prefill (same meaning as for pa_decode). */
+size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                          int32_t num_q_heads,
+                                          int32_t head_dim,
+                                          int32_t max_seq_len,
+                                          int32_t block_size,
+                                          int32_t kv_split_tokens);
+
+/*
+ * pa_chunked_prefill -- packed query chunks (and single decode rows) of
+ * several sequences against their paged context, causally.  Chunked prefill
+ * co-schedules prompt chunks with decode tokens ("Tech Radar: vLLM v1
+ * Production Engine Architecture ...", section "3. Dynamic Chunked
+ * Prefill"); the attention each row computes is the one of pa_decode with
+ * the row's own causal limit: row j of sequence s sits at position
+ * P = seq_lens[s] - q_len_s + j and sees keys 0..P.  Sequences with
+ * q_len == 1 are decode rows and may be mixed in freely.
+ * max_query_len must be >= every q_len and num_tokens == qsl[num_seqs].
+ */
+int pa_chunked_prefill(void* out, const void* query, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, int32_t num_seqs,
+                       int32_t num_tokens, int32_t max_seq_len,
+                       int32_t max_query_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, float scale,
+                       int32_t dtype, int32_t kv_split_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

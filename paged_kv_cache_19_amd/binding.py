@@ -1,0 +1,186 @@
+"""Thin ctypes binding of libpa (include/pa.h), same names as the C ABI.
+
+Argument marshalling only: every step of the path runs in libpa's HIP
+kernels.  torch supplies device memory (tensors are passed by data pointer)
+and the current HIP stream.  There is no fallback: if ``libpa.so`` is
+missing, or a call returns an error, a ``PAError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_F32 = 0
+PA_BF16 = 1
+
+STATUS = {
+    0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
+    -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_INDEX", -7: "PA_ERR_HIP",
+}
+
+# (name, restype, argtypes) of every symbol include/pa.h declares.
+_i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_version": (ctypes.c_int, []),
+    "pa_compute_slot_mapping": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_chunked_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_chunked_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                          _i32, _vp, _sz, _vp]),
+}
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (built in-tree); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PAError("load", -7) from FileNotFoundError(
+                f"{LIB_PATH} is missing: run `python -m paged_kv_cache_19_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PAError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libpa takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libpa takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def version() -> int:
+    return lib().pa_version()
+
+
+def compute_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                         query_start_loc: Optional[torch.Tensor], block_size: int,
+                         num_tokens: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    S = seq_lens.numel()
+    if num_tokens is None:
+        num_tokens = S if query_start_loc is None else int(query_start_loc[-1].item())
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=seq_lens.device)
+    _check("pa_compute_slot_mapping", lib().pa_compute_slot_mapping(
+        _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        _ptr(query_start_loc), S, num_tokens, block_size, _stream(stream)))
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    T, H, D = key.shape
+    NB, _, B, _ = k_cache.shape
+    _check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, H, D, B,
+        NB, _dtype(key), _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
+                           kv_split_tokens=0) -> int:
+    n = lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                        block_size, kv_split_tokens)
+    if n == 0:
+        raise PAError("pa_decode_workspace_bytes", -2)
+    return n
+
+
+def chunked_prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, head_dim, max_seq_len,
+                                    block_size, kv_split_tokens=0) -> int:
+    n = lib().pa_chunked_prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, head_dim,
+                                                 max_seq_len, block_size, kv_split_tokens)
+    if n == 0:
+        raise PAError("pa_chunked_prefill_workspace_bytes", -2)
+    return n
+
+
+def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+           kv_split_tokens: int = 0,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(S, Hq, D, max_seq_len, B, kv_split_tokens),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_decode", lib().pa_decode(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, Hkv, D, B, NB, scale,
+        _dtype(query), kv_split_tokens, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                    query_start_loc: torch.Tensor, max_seq_len: int, max_query_len: int,
+                    scale: float, kv_split_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, Hq, D = query.shape
+    NB, Hkv, B, _ = k_cache.shape
+    S = seq_lens.numel()
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:
+        workspace = torch.empty(chunked_prefill_workspace_bytes(S, T, Hq, D, max_seq_len, B,
+                                                                kv_split_tokens),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_chunked_prefill", lib().pa_chunked_prefill(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), _ptr(query_start_loc), S, T, max_seq_len,
+        max_query_len, Hq, Hkv, D, B, NB, scale, _dtype(query), kv_split_tokens,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

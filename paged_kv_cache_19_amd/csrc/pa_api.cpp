@@ -1,0 +1,302 @@
+// C ABI of libpa: argument validation, split planning, optional metadata
+// checks (PA_CHECK=1) and dispatch to the HIP kernels.  See include/pa.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kDefaultSplitTokens = 512;
+constexpr size_t kAlign = 256;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int log2i(int x) { return __builtin_ctz((unsigned)x); }
+
+bool check_enabled() {
+  const char* v = getenv("PA_CHECK");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// Keys one split covers.  0 selects the default; otherwise a multiple of 64
+// that keeps one split within 64 blocks (the MFMA kernel stages one block id
+// per lane).
+int split_tokens_for(int requested, int block_size) {
+  const int cap = 64 * (block_size > 8 ? block_size : 8);
+  if (requested == 0) return kDefaultSplitTokens < cap ? kDefaultSplitTokens : cap;
+  if (requested < 0 || requested % 64 != 0 || requested > cap) return -1;
+  return requested;
+}
+
+int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size, int dtype) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!is_pow2(block_size) || block_size > 64) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+struct WorkspacePlan {
+  int split_tokens = 0;
+  int max_splits = 0;
+  size_t part_o_bytes = 0;
+  size_t total = 0;
+};
+
+bool plan_workspace(int num_rows_tokens, int num_q_heads, int head_dim, int max_seq_len,
+                    int block_size, int kv_split_tokens, WorkspacePlan* p) {
+  if (num_rows_tokens < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 ||
+      !is_pow2(block_size) || block_size > 64)
+    return false;
+  const int st = split_tokens_for(kv_split_tokens, block_size);
+  if (st <= 0) return false;
+  p->split_tokens = st;
+  p->max_splits = (max_seq_len + st - 1) / st;
+  const size_t rows = (size_t)num_rows_tokens * num_q_heads * p->max_splits;
+  p->part_o_bytes = align_up(rows * head_dim * sizeof(float));
+  p->total = p->part_o_bytes + align_up(rows * 2 * sizeof(float));
+  if (p->total == 0) p->total = kAlign;
+  return true;
+}
+
+// Host-side validation of device metadata (PA_CHECK=1).  Synchronous.
+int validate_metadata(const int32_t* d_bt, int max_blocks, const int32_t* d_lens,
+                      const int32_t* d_qsl, int num_seqs, int num_tokens, int max_seq_len,
+                      int max_query_len, int block_size, int num_blocks, hipStream_t st) {
+  std::vector<int32_t> bt((size_t)num_seqs * max_blocks), lens(num_seqs), qsl(num_seqs + 1);
+  if (hipMemcpyAsync(bt.data(), d_bt, bt.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(lens.data(), d_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess)
+    return PA_ERR_HIP;
+  if (d_qsl) {
+    if (hipMemcpyAsync(qsl.data(), d_qsl, qsl.size() * 4, hipMemcpyDeviceToHost, st) !=
+        hipSuccess)
+      return PA_ERR_HIP;
+  } else {
+    for (int s = 0; s <= num_seqs; ++s) qsl[s] = s;
+  }
+  if (hipStreamSynchronize(st) != hipSuccess) return PA_ERR_HIP;
+  if (qsl[0] != 0 || qsl[num_seqs] != num_tokens) return PA_ERR_INDEX;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int L = lens[s];
+    const int qn = qsl[s + 1] - qsl[s];
+    if (qn < 0 || qn > max_query_len) return PA_ERR_INDEX;
+    if (L < 1 || L > max_seq_len || (int64_t)L > (int64_t)max_blocks * block_size)
+      return PA_ERR_INDEX;
+    if (qn > L) return PA_ERR_INDEX;
+    const int nb = (L + block_size - 1) / block_size;
+    for (int b = 0; b < nb; ++b) {
+      const int id = bt[(size_t)s * max_blocks + b];
+      if (id < 0 || id >= num_blocks) return PA_ERR_INDEX;
+    }
+  }
+  return PA_OK;
+}
+
+int validate_slots(const int64_t* d_slots, int num_tokens, int64_t num_slots, hipStream_t st) {
+  std::vector<int64_t> slots(num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (hipMemcpyAsync(slots.data(), d_slots, slots.size() * 8, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  std::vector<int64_t> valid;
+  for (int64_t s : slots) {
+    if (s >= num_slots) return PA_ERR_INDEX;
+    if (s >= 0) valid.push_back(s);
+  }
+  std::sort(valid.begin(), valid.end());
+  for (size_t i = 1; i < valid.size(); ++i)
+    if (valid[i] == valid[i - 1]) return PA_ERR_INDEX;
+  return PA_OK;
+}
+
+int attention_common(void* out, const void* query, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+                     const int32_t* qsl, int num_seqs, int num_tokens, int max_seq_len,
+                     int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int num_blocks, float scale, int dtype, int kv_split_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks <= 0 || num_blocks <= 0 ||
+      max_seq_len <= 0 || max_query_len <= 0 || !isfinite(scale))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
+  if ((int64_t)num_seqs * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  WorkspacePlan plan;
+  if (!plan_workspace(num_tokens, num_q_heads, head_dim, max_seq_len, block_size,
+                      kv_split_tokens, &plan))
+    return PA_ERR_SHAPE;
+  if (!workspace) return PA_ERR_WORKSPACE;
+  if (workspace_bytes < plan.total) return PA_ERR_WORKSPACE;
+  pa::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.bf16 = dtype == PA_BF16;
+  const int G = num_q_heads / num_kv_heads;
+  const bool mfma = a.bf16 && block_size >= 8;
+  const int64_t tiles_y = mfma ? ((int64_t)max_query_len * G + 63) / 64 : max_query_len;
+  if (tiles_y > 65535) return PA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    rc = validate_metadata(block_tables, max_blocks, seq_lens, qsl, num_seqs, num_tokens,
+                           max_seq_len, max_query_len, block_size, num_blocks, st);
+    if (rc != PA_OK) return rc;
+  }
+  a.q = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = qsl;
+  a.out = out;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_bytes);
+  a.max_blocks = max_blocks;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.log2_block = log2i(block_size);
+  a.num_blocks = num_blocks;
+  a.split_tokens = plan.split_tokens;
+  a.max_splits = plan.max_splits;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return pa::launch_attention(a, qsl != nullptr && max_query_len > 1, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size or count is out of range";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown dtype";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape not implemented";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_INDEX: return "PA_ERR_INDEX: device metadata out of range (PA_CHECK)";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_version(void) { return 100; }
+
+int pa_compute_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            const int32_t* query_start_loc, int32_t num_seqs,
+                            int32_t num_tokens, int32_t block_size, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 64) return PA_ERR_UNSUPPORTED;
+  if (!query_start_loc && num_tokens != num_seqs) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !block_tables || !seq_lens) return PA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    // Table entries are checked against no pool size here (slots only).
+    int rc = validate_metadata(block_tables, max_blocks_per_seq, seq_lens, query_start_loc,
+                               num_seqs, num_tokens, 1 << 30, 1 << 30, block_size,
+                               1 << 30, st);
+    if (rc != PA_OK) return rc;
+  }
+  return pa::launch_slot_mapping(slot_mapping, block_tables, max_blocks_per_seq, seq_lens,
+                                 query_start_loc, num_seqs, num_tokens, block_size,
+                                 st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!is_pow2(block_size) || block_size > 64) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    int rc = validate_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size, st);
+    if (rc != PA_OK) return rc;
+  }
+  return pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                      num_kv_heads, head_dim, block_size, num_blocks,
+                                      dtype == PA_BF16 ? 2 : 4, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t block_size,
+                                 int32_t kv_split_tokens) {
+  WorkspacePlan p;
+  if (!plan_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
+                      kv_split_tokens, &p))
+    return 0;
+  return p.total;
+}
+
+int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+              int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+              int32_t dtype, int32_t kv_split_tokens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                          kv_split_tokens, workspace, workspace_bytes, stream);
+}
+
+size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                          int32_t num_q_heads, int32_t head_dim,
+                                          int32_t max_seq_len, int32_t block_size,
+                                          int32_t kv_split_tokens) {
+  (void)num_seqs;
+  WorkspacePlan p;
+  if (!plan_workspace(num_tokens, num_q_heads, head_dim, max_seq_len, block_size,
+                      kv_split_tokens, &p))
+    return 0;
+  return p.total;
+}
+
+int pa_chunked_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                       int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                       int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                       int32_t dtype, int32_t kv_split_tokens, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && num_tokens > 0 && !query_start_loc) return PA_ERR_NULL;
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          seq_lens, query_start_loc, num_seqs, num_tokens, max_seq_len,
+                          max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                          num_blocks, scale, dtype, kv_split_tokens, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (pa_api.cpp) and the HIP
+// kernels (pa_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one attention launch needs.  Pointers are device pointers;
+// element pointers are raw bits (bf16 as uint16_t, fp32 as float).
+struct AttnArgs {
+  const void* q;            // [T, Hq, D]
+  const void* k_cache;      // [NB, Hkv, B, D]
+  const void* v_cache;      // [NB, Hkv, D, B]
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;  // nullptr: one row per sequence
+  void* out;                // [T, Hq, D]
+  float* part_o;            // [T * Hq, max_splits, D]
+  float* part_ml;           // [T * Hq, max_splits, 2]  (max in log2 units, sum)
+  int32_t max_blocks;
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
+  int32_t block_size, log2_block, num_blocks;
+  int32_t split_tokens, max_splits, max_query_len;
+  float scale_log2;         // scale * log2(e)
+  int32_t bf16;             // 1: bf16 elements, 0: fp32
+};
+
+// Which sequences a launch serves (chunked prefill runs a wide-tile kernel
+// for chunks and a narrow one for single-token rows).
+enum RowFilter : int32_t { kAllSeqs = 0, kMultiRowSeqs = 1, kSingleRowSeqs = 2 };
+
+hipError_t launch_slot_mapping(int64_t* slots, const int32_t* bt, int32_t max_blocks,
+                               const int32_t* seq_lens, const int32_t* qsl,
+                               int32_t num_seqs, int32_t num_tokens, int32_t block_size,
+                               hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slots,
+                                    int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t elem_bytes,
+                                    hipStream_t stream);
+
+// Split-K attention pass (writes final rows for single-split rows and
+// partials otherwise), then the log-sum-exp merge pass when needed.
+hipError_t launch_attention(const AttnArgs& a, bool has_chunks, hipStream_t stream);
+
+// True when the MFMA kernels serve this shape (bf16, B >= 8, D in {64,128}).
+bool mfma_path(const AttnArgs& a);
+
+}  // namespace pa

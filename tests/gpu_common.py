@@ -1,0 +1,121 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import math
+import random
+from typing import List, Optional, Sequence
+
+import torch
+
+import oracle.paged_attention as ref
+from paged_kv_cache_19_amd import binding, workloads
+
+TOL = {workloads.F32: 1e-4, workloads.BF16: 2e-2}
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def context_mask(wl: workloads.Workload) -> torch.Tensor:
+    """bool [NB, B]: slots holding a cached position (before this step's
+    tokens).  Everything else is poisoned with NaN before a GPU run."""
+    B = wl.shape.block_size
+    mask = torch.zeros(wl.num_blocks, B, dtype=torch.bool)
+    for s, row in enumerate(wl.block_tables):
+        ctx = wl.seq_lens[s] - wl.q_lens[s]
+        for lb, blk in enumerate(row):
+            n = min(B, ctx - lb * B)
+            if n > 0:
+                mask[blk, :n] = True
+    return mask
+
+
+def poison(wl: workloads.Workload) -> None:
+    mask = context_mask(wl).to(wl.device)
+    kc, vc = wl.tensors["k_cache"], wl.tensors["v_cache"]
+    kc.permute(0, 2, 1, 3)[~mask] = math.nan
+    vc.permute(0, 3, 1, 2)[~mask] = math.nan
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def sample_rows(wl: workloads.Workload, max_seqs: Optional[int], seed: int = 0) -> List[int]:
+    """Packed row indices to check against the oracle: every row of up to
+    ``max_seqs`` sequences (always the shortest and the longest), and for
+    query chunks the first/last rows, rows around block boundaries and a
+    random handful."""
+    rng = random.Random(seed)
+    S = wl.num_seqs
+    qsl = wl.query_start_loc()
+    if max_seqs is None or max_seqs >= S:
+        seqs = list(range(S))
+    else:
+        lens = wl.seq_lens
+        seqs = {lens.index(min(lens)), lens.index(max(lens))}
+        seqs |= set(rng.sample(range(S), max_seqs - 2))
+        seqs = sorted(seqs)
+    rows = []
+    B = wl.shape.block_size
+    for s in seqs:
+        n = wl.q_lens[s]
+        if n <= 48:
+            rows += list(range(qsl[s], qsl[s] + n))
+            continue
+        pick = {0, 1, 2, n - 3, n - 2, n - 1}
+        ctx = wl.seq_lens[s] - n
+        for j in range(n):
+            if (ctx + j) % B in (0, B - 1) and rng.random() < 0.3:
+                pick.add(j)
+        pick |= set(rng.sample(range(n), 8))
+        rows += [qsl[s] + j for j in sorted(pick)]
+    return rows
+
+
+def run_and_compare(wl: workloads.Workload, kv_split_tokens: int = 0,
+                    max_seqs: Optional[int] = None, do_poison: bool = True,
+                    force_chunked: bool = False):
+    """Full hot path on the GPU (slot mapping, cache write, attention) and the
+    oracle on copies of the same inputs.  Returns (out_gpu, max_abs_err)."""
+    shp = wl.shape
+    B = shp.block_size
+    dev = wl.device
+    t = wl.tensors
+    if do_poison:
+        poison(wl)
+    bt = wl.block_tables_tensor(dev)
+    lens = wl.seq_lens_tensor(dev)
+    decode_only = all(n == 1 for n in wl.q_lens) and not force_chunked
+    qsl = None if decode_only else wl.query_start_loc_tensor(dev)
+
+    kc0, vc0 = t["k_cache"].cpu(), t["v_cache"].cpu()
+    slots_ref = ref.compute_slot_mapping(bt.cpu(), wl.seq_lens,
+                                         None if qsl is None else wl.query_start_loc(), B)
+    slots = binding.compute_slot_mapping(bt, lens, qsl, B, num_tokens=wl.num_tokens)
+    torch.cuda.synchronize()
+    assert torch.equal(slots.cpu(), slots_ref), "slot mapping differs"
+
+    binding.reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], slots)
+    kc_ref, vc_ref = ref.reshape_and_cache(kc0, vc0, t["key"].cpu(), t["value"].cpu(), slots_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(t["k_cache"].cpu()), bits(kc_ref)), "K cache differs"
+    assert torch.equal(bits(t["v_cache"].cpu()), bits(vc_ref)), "V cache differs"
+
+    if decode_only:
+        out = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens,
+                             wl.max_seq_len, wl.scale, kv_split_tokens=kv_split_tokens)
+    else:
+        out = binding.chunked_prefill(t["query"], t["k_cache"], t["v_cache"], bt, lens, qsl,
+                                      wl.max_seq_len, wl.max_query_len, wl.scale,
+                                      kv_split_tokens=kv_split_tokens)
+    torch.cuda.synchronize()
+    out_cpu = out.cpu()
+    assert torch.isfinite(out_cpu.float()).all(), "non-finite output (poison reached out?)"
+    rows = sample_rows(wl, max_seqs)
+    expect = ref.paged_attention(t["query"].cpu(), kc_ref, vc_ref, bt.cpu(), wl.seq_lens,
+                                 wl.query_start_loc(), wl.scale, rows=rows)
+    err = (out_cpu[rows].double() - expect[rows]).abs().max().item()
+    return out, err

@@ -1,0 +1,111 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/pa.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_19_amd import binding
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pa.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from paged_kv_cache_19_amd import build
+        build.build()
+    os.environ.pop("PA_CHECK", None)
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    for code, name in binding.STATUS.items():
+        assert binding.status_string(code).startswith(name)
+    assert binding.status_string(12345) == "unknown pa_status"
+    assert binding.version() == 100
+
+
+def test_workspace_queries(lib):
+    n = lib.pa_decode_workspace_bytes(128, 64, 128, 8192, 16, 512)
+    splits = 16
+    assert n == 128 * 64 * splits * 128 * 4 + 128 * 64 * splits * 2 * 4
+    assert lib.pa_decode_workspace_bytes(128, 64, 128, 8192, 16, 0) == n
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 4, 0) > 0
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 3, 0) == 0       # B not a power of 2
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 100) == 0    # split not % 64
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 2048) == 0   # split > 64 blocks
+    assert lib.pa_decode_workspace_bytes(4, 8, 64, 0, 16, 0) == 0
+    assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 0) > 0
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, maxb=4, lens=FAKE, S=2, maxlen=64,
+             Hq=8, Hkv=2, D=128, B=16, NB=8, scale=0.1, dtype=1, split=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["lens"],
+                         a["S"], a["maxlen"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+                         a["scale"], a["dtype"], a["split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), -1), (dict(q=None), -1), (dict(kc=None), -1), (dict(bt=None), -1),
+    (dict(lens=None), -1), (dict(dtype=7), -3), (dict(Hq=6, Hkv=4), -2),
+    (dict(Hq=34, Hkv=2), -4), (dict(D=96), -4), (dict(B=12), -4), (dict(B=128), -4),
+    (dict(maxb=0), -2), (dict(NB=0), -2), (dict(maxlen=0), -2), (dict(scale=float("nan")), -2),
+    (dict(split=96), -2), (dict(ws=None), -5), (dict(wsb=16), -5), (dict(S=70000), -4),
+])
+def test_decode_rejects_bad_arguments(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _decode(lib, S=0, out=None) == 0
+
+
+def test_other_entry_points_reject_bad_arguments(lib):
+    # slot mapping
+    assert lib.pa_compute_slot_mapping(None, FAKE, 4, FAKE, None, 2, 2, 16, None) == -1
+    assert lib.pa_compute_slot_mapping(FAKE, FAKE, 4, FAKE, None, 2, 3, 16, None) == -2
+    assert lib.pa_compute_slot_mapping(FAKE, FAKE, 4, FAKE, None, 2, 2, 24, None) == -4
+    assert lib.pa_compute_slot_mapping(FAKE, FAKE, 0, FAKE, None, 2, 2, 16, None) == -2
+    assert lib.pa_compute_slot_mapping(None, None, 4, None, None, 0, 0, 16, None) == 0
+    # cache write
+    rc = lib.pa_reshape_and_cache
+    assert rc(FAKE, FAKE, FAKE, FAKE, None, 4, 2, 128, 16, 8, 1, None) == -1
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 5, None) == -3
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 80, 16, 8, 1, None) == -4
+    assert rc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 16, 8, 1, None) == -2
+    assert rc(None, None, None, None, None, 0, 2, 128, 16, 8, 1, None) == 0
+    # chunked prefill: query_start_loc is required
+    cp = lib.pa_chunked_prefill
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, 2, 10, 64, 8, 8, 2, 128, 16, 8, 0.1, 1,
+            0, FAKE, 1 << 30, None]
+    assert cp(*args) == -1
+    args[7] = FAKE
+    args[20] = None
+    assert cp(*args) == -5
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding.compute_slot_mapping(t.view(2, 2), t[:2], None, 16)

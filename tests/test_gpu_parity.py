@@ -1,0 +1,156 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Slot mapping and the cache write must match bit for bit; attention outputs
+must match within 1e-4 (fp32) / 2e-2 (bf16) max-abs error on every sampled
+row.  Every slot that does not hold a cached position (block tails, spare
+blocks, this step's slots before the write) is NaN-poisoned first, and table
+padding points at a poisoned spare block: a finite output proves none of it
+was read.
+"""
+import math
+
+import pytest
+import torch
+
+from paged_kv_cache_19_amd import binding, workloads
+from tests.gpu_common import TOL, log, run_and_compare
+
+pytestmark = pytest.mark.gpu
+
+FULL_SIZE_SEQ_SAMPLE = {1: None, 2: None, 3: 12, 4: 16, 5: None}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_parity(cfg):
+    log(f"[parity] workload {cfg}: {workloads.SHAPES[cfg].name}")
+    wl = workloads.make_workload(cfg, device="cuda")
+    out, err = run_and_compare(wl, max_seqs=FULL_SIZE_SEQ_SAMPLE[cfg])
+    log(f"[parity] workload {cfg}: max abs err {err:.3e}")
+    assert err <= TOL[wl.shape.dtype]
+    del wl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("split", [64, 128, 512, 1024])
+def test_split_counts_agree(split):
+    wl = workloads.make_workload(2, device="cuda", seq_lens=[1, 63, 64, 65, 700, 2048, 4000, 4096],
+                                 q_lens=[1] * 8)
+    log(f"[split] kv_split_tokens={split}")
+    out, err = run_and_compare(wl, kv_split_tokens=split)
+    assert err <= TOL[wl.shape.dtype]
+
+
+EDGE = [
+    # dtype, Hq, Hkv, D, B, seq_lens, q_lens
+    ("bf16", 32, 8, 128, 16, [1, 2, 15, 16, 17, 31, 32, 33], None),
+    ("bf16", 16, 16, 128, 16, [100, 37], None),                  # G = 1
+    ("bf16", 16, 1, 128, 16, [300, 5], None),                    # G = 16
+    ("bf16", 8, 2, 64, 16, [129, 64, 1], None),                  # head_dim 64
+    ("bf16", 8, 2, 128, 8, [77, 8, 9], None),                    # B = 8
+    ("bf16", 8, 2, 128, 32, [77, 32, 33, 1000], None),           # B = 32
+    ("bf16", 8, 2, 128, 64, [3000, 64, 65], None),               # B = 64
+    ("bf16", 8, 2, 128, 4, [77, 5, 4], None),                    # B = 4: vector-ALU path
+    ("bf16", 8, 2, 64, 1, [9, 1], None),                         # B = 1
+    ("f32", 8, 2, 128, 16, [100, 1, 530], None),                 # fp32 with B = 16
+    ("f32", 8, 4, 64, 2, [7, 40], None),
+    ("bf16", 32, 8, 128, 16, [600, 17, 9], [600, 5, 1]),         # pure prefill + chunk + decode
+    ("bf16", 8, 2, 128, 16, [40, 2000, 1], [33, 130, 1]),        # ragged chunks
+    ("bf16", 16, 1, 64, 32, [300, 260], [100, 3]),               # G = 16 chunks
+    ("f32", 8, 2, 64, 4, [50, 12, 64], [20, 12, 1]),             # fp32 chunks
+    ("bf16", 8, 2, 128, 4, [50, 12], [20, 1]),                   # bf16 chunks, B = 4
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"edge{i}" for i in range(len(EDGE))])
+def test_edge_shapes(case):
+    dtype, Hq, Hkv, D, B, lens, qls = case
+    shape = workloads.Shape("edge", dtype, Hq, Hkv, D, B)
+    wl = workloads.make_workload(2, seed=77, device="cuda", seq_lens=lens, q_lens=qls, shape=shape)
+    log(f"[edge] {case}")
+    out, err = run_and_compare(wl, force_chunked=qls is not None)
+    log(f"[edge] max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_decode_through_chunked_entry_point():
+    """q_len = 1 rows give the same result through pa_chunked_prefill."""
+    wl = workloads.make_workload(2, device="cuda", seq_lens=[300, 1, 4096, 17], q_lens=[1] * 4)
+    out, err = run_and_compare(wl, force_chunked=True)
+    assert err <= 2e-2
+
+
+def test_block_relabelling_gives_bit_identical_output():
+    wl = workloads.make_workload(2, device="cuda", seq_lens=[513, 2048, 33, 4000, 1000, 16],
+                                 q_lens=[1] * 6)
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    lens = wl.seq_lens_tensor("cuda")
+    out1 = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len, wl.scale)
+    perm = torch.randperm(wl.num_blocks, generator=torch.Generator().manual_seed(5)).cuda()
+    kc = torch.empty_like(t["k_cache"]); vc = torch.empty_like(t["v_cache"])
+    kc[perm] = t["k_cache"]; vc[perm] = t["v_cache"]
+    out2 = binding.decode(t["query"], kc, vc, perm[bt.long()].int().contiguous(), lens,
+                          wl.max_seq_len, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("where", ["first", "boundary", "tail"])
+def test_needle_is_found(where):
+    """One key per sequence is made to dominate; the output must be that
+    key's value row (an O(1) error if the block holding it were missed)."""
+    lens = [1000, 257, 4096, 33]
+    wl = workloads.make_workload(2, device="cuda", seq_lens=lens, q_lens=[1] * 4)
+    t = wl.tensors
+    B = wl.shape.block_size
+    G = wl.shape.num_q_heads // wl.shape.num_kv_heads
+    needles = []
+    for s, L in enumerate(lens):
+        p = {"first": 0, "boundary": (L // 2) // B * B, "tail": L - 2}[where]
+        blk = wl.block_tables[s][p // B]
+        for h in range(wl.shape.num_kv_heads):
+            qvec = t["query"][s, h * G:(h + 1) * G].float().sum(0)
+            t["k_cache"][blk, h, p % B] = (qvec / qvec.norm() * 60).to(torch.bfloat16)
+        needles.append((s, blk, p))
+    bt = wl.block_tables_tensor("cuda")
+    out = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, wl.seq_lens_tensor("cuda"),
+                         wl.max_seq_len, wl.scale)
+    torch.cuda.synchronize()
+    for s, blk, p in needles:
+        for h in range(wl.shape.num_kv_heads):
+            v = t["v_cache"][blk, h, :, p % B].float()
+            got = out[s, h * G:(h + 1) * G].float()
+            assert (got - v).abs().max().item() < 0.1, (s, h, where)
+
+
+def test_pa_check_reports_bad_metadata(monkeypatch):
+    monkeypatch.setenv("PA_CHECK", "1")
+    wl = workloads.make_workload(2, device="cuda", seq_lens=[40, 20], q_lens=[1, 1])
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    lens = wl.seq_lens_tensor("cuda")
+    binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len, wl.scale)
+    bad = bt.clone()
+    bad[0, 1] = wl.num_blocks + 5
+    with pytest.raises(binding.PAError) as e:
+        binding.decode(t["query"], t["k_cache"], t["v_cache"], bad, lens, wl.max_seq_len, wl.scale)
+    assert e.value.status == -6
+    with pytest.raises(binding.PAError) as e:       # a length beyond max_seq_len
+        binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, 30, wl.scale)
+    assert e.value.status == -6
+    dup = torch.tensor([5, 5], dtype=torch.int64, device="cuda")
+    with pytest.raises(binding.PAError) as e:
+        binding.reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], dup)
+    assert e.value.status == -6
+
+
+def test_negative_slots_are_skipped():
+    wl = workloads.make_workload(2, device="cuda", seq_lens=[40, 20], q_lens=[1, 1])
+    t = wl.tensors
+    before_k = t["k_cache"].clone()
+    before_v = t["v_cache"].clone()
+    slots = torch.tensor([-1, -7], dtype=torch.int64, device="cuda")
+    binding.reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], slots)
+    torch.cuda.synchronize()
+    assert torch.equal(before_k.view(torch.int16), t["k_cache"].view(torch.int16))
+    assert torch.equal(before_v.view(torch.int16), t["v_cache"].view(torch.int16))
