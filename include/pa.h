@@ -51,8 +51,7 @@
  *
  * Supported: dtype PA_F32 or PA_BF16; head_dim 64 or 128; block_size a
  * power of two from 1 to 64; H_q % H_kv == 0 with 1 <= H_q / H_kv <= 16;
- * kv_split_tokens 0 (auto) or a multiple of 64 with
- * kv_split_tokens <= 64 * max(block_size, 8).
+ * kv_split_tokens 0 (auto) or a positive multiple of 64.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -117,10 +116,13 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
                          int32_t num_blocks, int32_t dtype, void* stream);
 
 /*
- * Workspace for pa_decode: split-K partial results (running max, sum and
- * unnormalised output per query row and context split).  kv_split_tokens is
- * the number of keys one split covers (0 = the library chooses); pass the
- * same value to pa_decode.  Returns 0 for invalid arguments.
+ * Workspace for pa_decode: partial results (running max, sum and
+ * unnormalised output) of the pieces a row's keys are cut into, plus a small
+ * header.  kv_split_tokens: 0 lets the library balance the work over the
+ * GPU (every resident wave streams an equal share of all keys); a positive
+ * multiple of 64 cuts every sequence into fixed splits of that many keys
+ * instead.  Pass the same value to pa_decode.  Returns 0 for invalid
+ * arguments.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t head_dim, int32_t max_seq_len,
@@ -133,9 +135,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * "Physical Block Mapping and Kernel Invocation".
  *   out[s][h] = softmax_t(scale * query[s][h] . K_s[t][h/G]) . V_s[t][h/G],
  *   t = 0 .. seq_lens[s]-1, K_s/V_s gathered through block_tables[s].
- * max_seq_len must be >= every seq_len.  Long contexts are cut into splits
- * of kv_split_tokens keys whose partial results are merged exactly
- * (log-sum-exp) in a second pass.
+ * max_seq_len must be >= every seq_len.  Keys of one row may be cut into
+ * pieces (see pa_decode_workspace_bytes); their partial results are merged
+ * exactly (log-sum-exp) in a second pass.
  */
 int pa_decode(void* out, const void* query, const void* k_cache,
               const void* v_cache, const int32_t* block_tables,

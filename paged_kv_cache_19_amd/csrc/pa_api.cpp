@@ -15,6 +15,8 @@
 namespace {
 
 constexpr int kDefaultSplitTokens = 512;
+// The balanced decode keeps every sequence's step prefix sum in LDS.
+constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kAlign = 256;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -26,13 +28,12 @@ bool check_enabled() {
   return v && v[0] && strcmp(v, "0") != 0;
 }
 
-// Keys one split covers.  0 selects the default; otherwise a multiple of 64
-// that keeps one split within 64 blocks (the MFMA kernel stages one block id
-// per lane).
+// Keys one split covers on the fixed-split path: 0 selects the default,
+// otherwise a positive multiple of 64.
 int split_tokens_for(int requested, int block_size) {
-  const int cap = 64 * (block_size > 8 ? block_size : 8);
-  if (requested == 0) return kDefaultSplitTokens < cap ? kDefaultSplitTokens : cap;
-  if (requested < 0 || requested % 64 != 0 || requested > cap) return -1;
+  (void)block_size;
+  if (requested == 0) return kDefaultSplitTokens;
+  if (requested < 0 || requested % 64 != 0) return -1;
   return requested;
 }
 
@@ -48,24 +49,40 @@ int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size
 }
 
 struct WorkspacePlan {
-  int split_tokens = 0;
-  int max_splits = 0;
+  int split_tokens = 0;   // fixed-split path: keys per split
+  int max_splits = 0;     // fixed-split path: partial slots per row
+  int max_pieces = 0;     // balanced decode: partial slots per row (0: unused)
+  int slots = 0;          // partial slots per row reserved in the workspace
   size_t part_o_bytes = 0;
+  size_t part_ml_bytes = 0;
+  size_t header_bytes = 0;
   size_t total = 0;
 };
 
-bool plan_workspace(int num_rows_tokens, int num_q_heads, int head_dim, int max_seq_len,
-                    int block_size, int kv_split_tokens, WorkspacePlan* p) {
-  if (num_rows_tokens < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 ||
-      !is_pow2(block_size) || block_size > 64)
+// Workspace layout: part_o [rows, slots, D] fp32 | part_ml [rows, slots, 2]
+// fp32 | balanced-decode header (step total, wave count, per-sequence step
+// prefix sums).  rows = query tokens * query heads.
+bool plan_workspace(int num_rows_tokens, int num_seqs, int num_q_heads, int head_dim,
+                    int max_seq_len, int block_size, int kv_split_tokens, bool balanced_decode,
+                    WorkspacePlan* p) {
+  if (num_rows_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 ||
+      max_seq_len <= 0 || !is_pow2(block_size) || block_size > 64)
     return false;
   const int st = split_tokens_for(kv_split_tokens, block_size);
   if (st <= 0) return false;
   p->split_tokens = st;
   p->max_splits = (max_seq_len + st - 1) / st;
-  const size_t rows = (size_t)num_rows_tokens * num_q_heads * p->max_splits;
+  p->max_pieces = 0;
+  if (balanced_decode && kv_split_tokens == 0) {
+    const int steps = (max_seq_len + 31) / 32;
+    p->max_pieces = (steps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
+  }
+  p->slots = p->max_splits > p->max_pieces ? p->max_splits : p->max_pieces;
+  const size_t rows = (size_t)num_rows_tokens * num_q_heads * p->slots;
   p->part_o_bytes = align_up(rows * head_dim * sizeof(float));
-  p->total = p->part_o_bytes + align_up(rows * 2 * sizeof(float));
+  p->part_ml_bytes = align_up(rows * 2 * sizeof(float));
+  p->header_bytes = p->max_pieces ? align_up(16 + (size_t)(num_seqs + 1) * 4) : 0;
+  p->total = p->part_o_bytes + p->part_ml_bytes + p->header_bytes;
   if (p->total == 0) p->total = kAlign;
   return true;
 }
@@ -137,9 +154,10 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
   if ((int64_t)num_seqs * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   WorkspacePlan plan;
-  if (!plan_workspace(num_tokens, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, &plan))
+  if (!plan_workspace(num_tokens, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
+                      kv_split_tokens, qsl == nullptr, &plan))
     return PA_ERR_SHAPE;
+  if (plan.max_splits > 65535) return PA_ERR_UNSUPPORTED;
   if (!workspace) return PA_ERR_WORKSPACE;
   if (workspace_bytes < plan.total) return PA_ERR_WORKSPACE;
   pa::AttnArgs a;
@@ -174,12 +192,18 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   a.log2_block = log2i(block_size);
   a.num_blocks = num_blocks;
   a.split_tokens = plan.split_tokens;
-  a.max_splits = plan.max_splits;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return pa::launch_attention(a, qsl != nullptr && max_query_len > 1, st) == hipSuccess
-             ? PA_OK
-             : PA_ERR_HIP;
+  hipError_t err;
+  if (plan.max_pieces > 0 && pa::mfma_path(a) && num_seqs <= kMaxBalancedSeqs) {
+    a.max_splits = plan.max_pieces;
+    err = pa::launch_decode_streamk(
+        a, static_cast<char*>(workspace) + plan.part_o_bytes + plan.part_ml_bytes, st);
+  } else {
+    a.max_splits = plan.max_splits;
+    err = pa::launch_attention(a, qsl != nullptr && max_query_len > 1, st);
+  }
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
@@ -253,8 +277,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t max_seq_len, int32_t block_size,
                                  int32_t kv_split_tokens) {
   WorkspacePlan p;
-  if (!plan_workspace(num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, &p))
+  if (!plan_workspace(num_seqs, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
+                      kv_split_tokens, true, &p))
     return 0;
   return p.total;
 }
@@ -275,10 +299,9 @@ size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
                                           int32_t num_q_heads, int32_t head_dim,
                                           int32_t max_seq_len, int32_t block_size,
                                           int32_t kv_split_tokens) {
-  (void)num_seqs;
   WorkspacePlan p;
-  if (!plan_workspace(num_tokens, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, &p))
+  if (!plan_workspace(num_tokens, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
+                      kv_split_tokens, false, &p))
     return 0;
   return p.total;
 }

@@ -27,6 +27,10 @@ struct AttnArgs {
   int32_t bf16;             // 1: bf16 elements, 0: fp32
 };
 
+// Balanced decode: every resident wave streams at least this many 32-key
+// steps, which bounds the pieces one row can be cut into.
+constexpr int kMinStepsPerWave = 8;
+
 // Which sequences a launch serves (chunked prefill runs a wide-tile kernel
 // for chunks and a narrow one for single-token rows).
 enum RowFilter : int32_t { kAllSeqs = 0, kMultiRowSeqs = 1, kSingleRowSeqs = 2 };
@@ -46,6 +50,11 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 // Split-K attention pass (writes final rows for single-split rows and
 // partials otherwise), then the log-sum-exp merge pass when needed.
 hipError_t launch_attention(const AttnArgs& a, bool has_chunks, hipStream_t stream);
+
+// Balanced ("stream-K") decode over a fixed set of resident waves, then the
+// merge of the pieces.  ``header`` is workspace for the step prefix sums
+// (16 + 4 * (num_seqs + 1) bytes); a.max_splits is the piece capacity per row.
+hipError_t launch_decode_streamk(const AttnArgs& a, void* header, hipStream_t stream);
 
 // True when the MFMA kernels serve this shape (bf16, B >= 8, D in {64,128}).
 bool mfma_path(const AttnArgs& a);

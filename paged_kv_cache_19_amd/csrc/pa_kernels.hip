@@ -183,99 +183,165 @@ __global__ __launch_bounds__(16 * D * ES / 16) void reshape_and_cache_kernel(
 // tokens).  The PV B operand (32 tokens x 16 head_dim columns) is then one
 // 16-byte load per lane from the [D, B] V layout.  No LDS round trip.
 // ---------------------------------------------------------------------------
+// Cross-lane all-reduce over lanes l ^ 16 and l ^ 32 (the four lanes that
+// hold one query row in the MFMA accumulator layout), on the VALU
+// permlane-swap instructions of gfx950.  Each swap returns, in every lane,
+// the lane's own value and its partner's value (in some order), so a
+// symmetric combine of the pair is the butterfly step.
+__device__ __forceinline__ float xl_max(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+__device__ __forceinline__ float xl_sum(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// One step (32 keys) of K and V fragments in MFMA operand layout.
+template <int D>
+struct KVFrag {
+  bf16x8 ka[D / 32], kb[D / 32], v[D / 16];
+};
+
+// Rescaling of the running output is skipped while a chunk's maximum stays
+// within this many powers of two of the running maximum: the exponentials
+// are then at most 2^8 and the final o / l is unchanged.
+constexpr float kLazyRescaleLog2 = 8.f;
+
+// Query rows of one wave (R tiles of 16) and their online-softmax state.
 template <int D, int R>
-__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
-  constexpr int KK = D / 32;  // QK k-steps
-  constexpr int NT = D / 16;  // PV head_dim tiles
-  const int lane = threadIdx.x;
+struct RowState {
+  bf16x8 qf[R][D / 32];
+  int klim[R];
+  float m[R], l[R];
+  f32x4 o[R][D / 16];
+};
+
+// One sequence / KV head as the kernels address it.
+struct SeqView {
+  int s, kvh, L, r0, qn, nblk, kcap;
+};
+
+__device__ __forceinline__ SeqView seq_view(const AttnArgs& a, int s, int kvh, int L, int r0, int qn) {
+  SeqView v;
+  v.s = s;
+  v.kvh = kvh;
+  v.L = L;
+  v.r0 = r0;
+  v.qn = qn;
+  v.nblk = table_blocks(L, a.log2_block, a.max_blocks);
+  v.kcap = v.nblk << a.log2_block;
+  return v;
+}
+
+// Load the query rows row0 .. row0 + 16R - 1 of a sequence (row = j * G + g
+// for chunk token j and group head g) into B-operand fragments, and reset
+// the softmax state.  Rows past the sequence are zero and see no keys.
+template <int D, int R>
+__device__ __forceinline__ void load_rows(const AttnArgs& a, const SeqView& v, int row0,
+                                          RowState<D, R>& st) {
+  constexpr int KK = D / 32;
+  const int lane = threadIdx.x & 63;
   const int i = lane & 15;
   const int j4 = lane >> 4;
-  const int split = blockIdx.x;
-  const int tg = blockIdx.y;
-  const int s = blockIdx.z / a.num_kv_heads;
-  const int kvh = blockIdx.z - s * a.num_kv_heads;
-  const int T = a.num_tokens;
-
-  int r0, qn;
-  seq_rows(a.query_start_loc, s, T, r0, qn);
-  if (filter == kMultiRowSeqs && qn <= 1) return;
-  if (filter == kSingleRowSeqs && qn != 1) return;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int nrows = qn * G;
-  const int row0 = tg * 16 * R;
-  if (row0 >= nrows) return;
-  const int L = a.seq_lens[s];
-  const int lg = a.log2_block;
-  const int B = 1 << lg;
-  const int nblk = table_blocks(L, lg, a.max_blocks);
-  const int kcap = nblk << lg;
-  const int row_last = min(row0 + 16 * R, nrows) - 1;
-  const int kv_wave = min(L - qn + row_last / G + 1, kcap);
-  const int k_begin = split * a.split_tokens;
-  if (k_begin >= kv_wave) return;
-  const int k_end = min(k_begin + a.split_tokens, kv_wave);
-
-  // Block ids of this split, one logical block per lane (the split spans at
-  // most 64 blocks); clamped so that any table value stays inside the pool.
-  const int blk0 = k_begin >> lg;
-  int wid = a.block_tables[(int64_t)s * a.max_blocks + min(blk0 + lane, nblk - 1)];
-  wid = clampi(wid, 0, a.num_blocks - 1);
-
-  const int Hq = a.num_q_heads;
+  const int nrows = v.qn * G;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  int klim[R];
-  bf16x8 qf[R][KK];
 #pragma unroll
   for (int t = 0; t < R; ++t) {
     const int row = row0 + 16 * t + i;
-    klim[t] = 0;
+    st.klim[t] = 0;
     if (row < nrows) {
       const int j = row / G;
       const int g = row - j * G;
-      klim[t] = min(L - qn + j + 1, kcap);
-      const uint16_t* qp = q + ((int64_t)(r0 + j) * Hq + kvh * G + g) * D + 8 * j4;
+      st.klim[t] = min(v.L - v.qn + j + 1, v.kcap);
+      const uint16_t* qp =
+          q + ((int64_t)(v.r0 + j) * a.num_q_heads + v.kvh * G + g) * D + 8 * j4;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qf[t][kk] = load_bf16x8(qp + 32 * kk);
+      for (int kk = 0; kk < KK; ++kk) st.qf[t][kk] = load_bf16x8(qp + 32 * kk);
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qf[t][kk] = bf16x8{};
+      for (int kk = 0; kk < KK; ++kk) st.qf[t][kk] = bf16x8{};
     }
+    st.m[t] = neg_inf();
+    st.l[t] = 0.f;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) st.o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+}
 
-  float m[R], l[R];
-  f32x4 o[R][NT];
-#pragma unroll
-  for (int t = 0; t < R; ++t) {
-    m[t] = neg_inf();
-    l[t] = 0.f;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+// Stream keys [k_begin, k_end) of one sequence / KV head through the row
+// tiles, 32 keys per step with the next step's K/V loads in flight.
+//   kv_wave: one past the last key any row of the wave sees (keys from here
+//            on may be unwritten slots: their V is zeroed);
+//   kv_min:  keys below it are visible to every row (no mask needed).
+//
+// QK^T uses the 16x16x32 MFMA with A = K (16 token rows x 32 head_dim) and
+// B = Q^T (32 head_dim x 16 query rows), two MFMAs per step ("a" and "b").
+// MFMA row i of "a" is token 8*(i/4) + i%4 of the step and row i of "b" is
+// that token + 4, so the accumulator layout (lane l holds rows 4*(l/16)+r,
+// column l%16) leaves lane l with tokens 8*(l/16) .. 8*(l/16)+7 of query
+// row l%16: exactly the A operand of the PV MFMA (16 query rows x 32
+// tokens).  The PV B operand (32 tokens x 16 head_dim columns) is then one
+// 16-byte load per lane from the [D, B] V layout.  No LDS round trip.
+//
+// Block ids come from a window of 64 logical blocks held one per lane; a
+// step never straddles two windows (a window is 64*B keys, a multiple of
+// 32), and the next window is loaded one window ahead.
+template <int D, int R>
+__device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int kv_wave, int kv_min,
+                                       int k_begin, int k_end, RowState<D, R>& st) {
+  constexpr int KK = D / 32;
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15;
+  const int j4 = lane >> 4;
+  const int lg = a.log2_block;
+  const int B = 1 << lg;
+  const int64_t trow = (int64_t)v.s * a.max_blocks;
+  auto window = [&](int b0) {
+    const int x = a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)];
+    return clampi(x, 0, a.num_blocks - 1);
+  };
+  int blk0 = k_begin >> lg;
+  int wid = window(blk0);
+  int wid_next = window(blk0 + 64);
+  auto block_id = [&](int pos) { return __shfl(wid, min(pos >> lg, v.nblk - 1) - blk0); };
 
   const int64_t blk_stride = (int64_t)a.num_kv_heads * B * D;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * B * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D * B;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)v.kvh * B * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)v.kvh * D * B;
   const int tok_a = 8 * (i >> 2) + (i & 3);
   const float sl2 = a.scale_log2;
 
-  for (int c = k_begin; c < k_end; c += 32) {
+  auto load = [&](KVFrag<D>& f, int c) {
+    if ((c >> lg) - blk0 >= 64) {  // wave-uniform: enter the next window
+      blk0 += 64;
+      wid = wid_next;
+      wid_next = window(blk0 + 64);
+    }
     const int pa_ = c + tok_a;
     const int pb_ = pa_ + 4;
     const int pv_ = c + 8 * j4;
-    const int ia = __shfl(wid, min(pa_ >> lg, nblk - 1) - blk0);
-    const int ib = __shfl(wid, min(pb_ >> lg, nblk - 1) - blk0);
-    const int iv = __shfl(wid, min(pv_ >> lg, nblk - 1) - blk0);
-    const uint16_t* ka = kbase + ia * blk_stride + (pa_ & (B - 1)) * D + 8 * j4;
-    const uint16_t* kb = kbase + ib * blk_stride + (pb_ & (B - 1)) * D + 8 * j4;
-    const uint16_t* vp = vbase + iv * blk_stride + (int64_t)i * B + (pv_ & (B - 1));
-    bf16x8 kfa[KK], kfb[KK], vf[NT];
+    const uint16_t* ka = kbase + block_id(pa_) * blk_stride + (pa_ & (B - 1)) * D + 8 * j4;
+    const uint16_t* kb = kbase + block_id(pb_) * blk_stride + (pb_ & (B - 1)) * D + 8 * j4;
+    const uint16_t* vp = vbase + block_id(pv_) * blk_stride + (int64_t)i * B + (pv_ & (B - 1));
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      kfa[kk] = load_bf16x8(ka + 32 * kk);
-      kfb[kk] = load_bf16x8(kb + 32 * kk);
+      f.ka[kk] = load_bf16x8(ka + 32 * kk);
+      f.kb[kk] = load_bf16x8(kb + 32 * kk);
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n) vf[n] = load_bf16x8(vp + (int64_t)16 * n * B);
+    for (int n = 0; n < NT; ++n) f.v[n] = load_bf16x8(vp + (int64_t)16 * n * B);
+  };
+
+  auto compute = [&](KVFrag<D>& f, int c) {
+    const int pv_ = c + 8 * j4;
     if (c + 32 > kv_wave) {
       // Keys past the last visible one may be unwritten slots: zero their V
       // so that 0-weight * garbage cannot produce NaN.
@@ -283,71 +349,105 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
       for (int e = 0; e < 8; ++e) {
         if (pv_ + e >= kv_wave) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) vf[n][e] = static_cast<__bf16>(0.f);
+          for (int n = 0; n < NT; ++n) f.v[n][e] = static_cast<__bf16>(0.f);
         }
       }
     }
-
+    const bool need_mask = c + 32 > kv_min;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfa[kk], qf[t][kk], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfb[kk], qf[t][kk], sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.ka[kk], st.qf[t][kk], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kb[kk], st.qf[t][kk], sb, 0, 0, 0);
       }
       float sv[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sv[r] = sa[r];
-        sv[4 + r] = sb[r];
+        sv[r] = sa[r] * sl2;
+        sv[4 + r] = sb[r] * sl2;
       }
-      float mx = neg_inf();
+      if (need_mask) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = (pv_ + e < klim[t]) ? sv[e] * sl2 : neg_inf();
-        mx = fmaxf(mx, sv[e]);
+        for (int e = 0; e < 8; ++e) sv[e] = (pv_ + e < st.klim[t]) ? sv[e] : neg_inf();
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[t], mx);
-      const float muse = (mnew == neg_inf()) ? 0.f : mnew;
-      const float alpha = fast_exp2(m[t] - muse);
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = xl_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > st.m[t] + kLazyRescaleLog2) != 0) {
+        const float mnew = fmaxf(st.m[t], mx);
+        const float alpha = fast_exp2(st.m[t] - ((mnew == neg_inf()) ? 0.f : mnew));
+        st.l[t] *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * j4 + r);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st.o[t][n][r] *= ar[r];
+        st.m[t] = mnew;
+      }
+      const float muse = (st.m[t] == neg_inf()) ? 0.f : st.m[t];
       float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = fast_exp2(sv[e] - muse);
-        ps += sv[e];
-      }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l[t] = l[t] * alpha + ps;
-      m[t] = mnew;
-      float ar[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * j4 + r);
       bf16x8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(sv[e]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[t][n][r] *= ar[r];
-        o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf[n], o[t][n], 0, 0, 0);
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(sv[e] - muse);
+        ps += p;
+        pf[e] = static_cast<__bf16>(p);
       }
+      st.l[t] += xl_sum(ps);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        st.o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, f.v[n], st.o[t][n], 0, 0, 0);
     }
-  }
+  };
 
-  // Lane l holds output rows 4*(l/16)+r, head_dim columns 16*n + l%16.
-  const int ST = a.split_tokens;
+  // Two fragment sets, loaded one step ahead.  The last prefetch re-reads
+  // the final step (an L2 hit) so that every iteration issues the same loads
+  // and the wait counts stay exact.
+  KVFrag<D> f0, f1;
+  int c = k_begin;
+  load(f0, c);
+  while (true) {
+    load(f1, c + 32 < k_end ? c + 32 : c);
+    compute(f0, c);
+    c += 32;
+    if (c >= k_end) break;
+    load(f0, c + 32 < k_end ? c + 32 : c);
+    compute(f1, c);
+    c += 32;
+    if (c >= k_end) break;
+  }
+}
+
+// Write the wave's rows: normalised output when ``whole`` (this piece saw
+// every key of the row), else the piece's (o, m, l) into partial slot
+// ``slot`` of the row.  Lane l holds rows 4*(l/16)+r, columns 16*n + l%16.
+//
+// With ``split_tokens`` > 0 (fixed splits) the decision is made per row: a
+// row whose keys fit in one split is final, rows that see no key of this
+// split (k_begin) are skipped.
+template <int D, int R>
+__device__ __forceinline__ void write_rows(const AttnArgs& a, const SeqView& v, int row0,
+                                           const RowState<D, R>& st, bool whole, int slot,
+                                           int split_tokens = 0, int k_begin = 0) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15;
+  const int j4 = lane >> 4;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int nrows = v.qn * G;
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int t = 0; t < R; ++t) {
     float lr[4], mr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      lr[r] = __shfl(l[t], 4 * j4 + r);
-      mr[r] = __shfl(m[t], 4 * j4 + r);
+      lr[r] = __shfl(st.l[t], 4 * j4 + r);
+      mr[r] = __shfl(st.m[t], 4 * j4 + r);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -355,19 +455,23 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
       if (row >= nrows) continue;
       const int j = row / G;
       const int g = row - j * G;
-      const int kl = min(L - qn + j + 1, kcap);
-      if (kl <= k_begin) continue;
-      const int ns = min((kl + ST - 1) / ST, a.max_splits);
-      const int64_t orow = (int64_t)(r0 + j) * Hq + kvh * G + g;
-      if (ns == 1) {
+      const int64_t orow = (int64_t)(v.r0 + j) * a.num_q_heads + v.kvh * G + g;
+      bool final_row = whole;
+      if (split_tokens > 0) {
+        const int kl = min(v.L - v.qn + j + 1, v.kcap);
+        if (kl <= k_begin) continue;
+        final_row = min((kl + split_tokens - 1) / split_tokens, a.max_splits) == 1;
+      }
+      if (final_row) {
         const float inv = 1.f / lr[r];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) out[orow * D + 16 * n + i] = f32_to_bf16_bits(o[t][n][r] * inv);
+        for (int n = 0; n < NT; ++n) out[orow * D + 16 * n + i] = f32_to_bf16_bits(st.o[t][n][r] * inv);
       } else {
-        const int64_t pidx = orow * a.max_splits + split;
+        if (slot >= a.max_splits) continue;  // out-of-contract lengths: stay in bounds
+        const int64_t pidx = orow * a.max_splits + slot;
         float* po = a.part_o + pidx * D;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) po[16 * n + i] = o[t][n][r];
+        for (int n = 0; n < NT; ++n) po[16 * n + i] = st.o[t][n][r];
         if (i == 0) {
           a.part_ml[2 * pidx] = mr[r];
           a.part_ml[2 * pidx + 1] = lr[r];
@@ -375,6 +479,205 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-split bf16 attention: one wave per (sequence x KV head, row-tile
+// group, split of split_tokens keys).  Serves query chunks (R = 2) and
+// decode rows when a split size is given.
+// ---------------------------------------------------------------------------
+template <int D, int R>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
+  // Grid: x = (sequence, KV head) fastest, z = split.  Workgroups are dealt
+  // to the 8 XCDs round-robin by linear id, so this gives every XCD the same
+  // mix of sequences and splits (with the split fastest, XCD k would get
+  // split k of every sequence and the long-context tail would pile up on a
+  // few XCDs).
+  const int s = blockIdx.x / a.num_kv_heads;
+  const int kvh = blockIdx.x - s * a.num_kv_heads;
+  const int tg = blockIdx.y;
+  const int split = blockIdx.z;
+  const int L = a.seq_lens[s];
+  int r0, qn;
+  seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+  if (filter == kMultiRowSeqs && qn <= 1) return;
+  if (filter == kSingleRowSeqs && qn != 1) return;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int nrows = qn * G;
+  const int row0 = tg * 16 * R;
+  if (row0 >= nrows) return;
+  const SeqView v = seq_view(a, s, kvh, L, r0, qn);
+  // Rows are ordered by query position: the first row has the smallest key
+  // limit and the last row the largest.
+  const int row_last = min(row0 + 16 * R, nrows) - 1;
+  const int kv_wave = min(L - qn + row_last / G + 1, v.kcap);
+  const int kv_min = min(L - qn + row0 / G + 1, v.kcap);
+  const int k_begin = split * a.split_tokens;
+  if (k_begin >= kv_wave) return;
+  const int k_end = min(k_begin + a.split_tokens, kv_wave);
+  RowState<D, R> st;
+  load_rows<D, R>(a, v, row0, st);
+  attend<D, R>(a, v, kv_wave, kv_min, k_begin, k_end, st);
+  // A row whose keys span more than one split leaves a partial in slot
+  // ``split`` for the merge pass; the others are final here.
+  write_rows<D, R>(a, v, row0, st, false, split, a.split_tokens, k_begin);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced ("stream-K") bf16 decode.  The work is the list of 32-key steps
+// of every (sequence, KV head), sequence-major; a fixed number of resident
+// waves each take one contiguous, equal share of that list (at least
+// kMinStepsPerWave steps), so all waves stream the same number of bytes and
+// finish together.  A share may start or end inside a sequence; such pieces
+// leave (o, m, l) partials that the merge pass combines.  Every wave
+// rebuilds the per-sequence step prefix sums in LDS from seq_lens; wave 0
+// also stores them (with the step total and wave count) in the workspace
+// header for the merge pass.
+// ---------------------------------------------------------------------------
+struct StreamKHeader {
+  int64_t total_steps;
+  int64_t waves;
+  // followed by int32 prefix[num_seqs + 1]
+};
+
+__device__ __forceinline__ int64_t wave_of_step(int64_t g, int64_t waves, int64_t total) {
+  return ((g + 1) * waves - 1) / total;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_streamk_kernel(AttnArgs a, int waves,
+                                                            StreamKHeader* hdr) {
+  extern __shared__ int smem[];
+  const int S = a.num_seqs;
+  int* P = smem;           // [S + 1] steps before sequence s (per KV head)
+  int* Ls = smem + S + 1;  // [S]     sequence lengths
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x;
+  const int Hkv = a.num_kv_heads;
+  const int lg = a.log2_block;
+  for (int s = lane; s < S; s += 64) {
+    const int L = a.seq_lens[s];
+    const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
+    P[s + 1] = kl > 0 ? (kl + 31) >> 5 : 0;
+    Ls[s] = L;
+  }
+  __syncthreads();
+  {
+    const int k = (S + 63) >> 6;
+    const int lo = min(lane * k, S);
+    const int hi = min(lo + k, S);
+    int run = 0;
+    for (int s = lo; s < hi; ++s) {
+      run += P[s + 1];
+      P[s + 1] = run;
+    }
+    int incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int off = incl - run;
+    for (int s = lo; s < hi; ++s) P[s + 1] += off;
+    if (lane == 0) P[0] = 0;
+  }
+  __syncthreads();
+  const int64_t N = (int64_t)Hkv * P[S];
+  const int64_t weff = N == 0 ? 0 : min((int64_t)waves, max((int64_t)1, N / kMinStepsPerWave));
+  if (w == 0) {
+    if (lane == 0) {
+      hdr->total_steps = N;
+      hdr->waves = weff;
+    }
+    int* hp = reinterpret_cast<int*>(hdr + 1);
+    for (int s = lane; s <= S; s += 64) hp[s] = P[s];
+  }
+  if (w >= weff) return;
+  int64_t g = (int64_t)w * N / weff;
+  const int64_t g_end = (int64_t)(w + 1) * N / weff;
+
+  // Sequence holding step g: the largest s with Hkv * P[s] <= g.
+  int s;
+  {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)Hkv * P[mid] <= g) lo = mid;
+      else hi = mid - 1;
+    }
+    s = lo;
+  }
+  while (g < g_end) {
+    while ((int64_t)Hkv * P[s + 1] <= g) ++s;
+    const int nch = P[s + 1] - P[s];
+    const int64_t base = (int64_t)Hkv * P[s];
+    const int kvh = (int)((g - base) / nch);
+    const int c0 = (int)(g - base - (int64_t)kvh * nch);
+    const int c1 = (int)min((int64_t)nch, c0 + (g_end - g));
+    const int64_t g_item = base + (int64_t)kvh * nch;
+    const int64_t wf = wave_of_step(g_item, weff, N);
+    const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
+    const SeqView v = seq_view(a, s, kvh, Ls[s], s, 1);
+    const int kl = min(v.L, v.kcap);
+    RowState<D, 1> st;
+    load_rows<D, 1>(a, v, 0, st);
+    attend<D, 1>(a, v, kl, kl, c0 * 32, min(c1 * 32, kl), st);
+    write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf));
+    g += c1 - c0;
+  }
+}
+
+// Merge for the balanced decode: the pieces of row (s, h) are the waves whose
+// shares intersect the row's step range.
+template <int ES, int D>
+__global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const StreamKHeader* hdr) {
+  constexpr int DD = D / 64;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + wave;
+  const int s = blockIdx.y;
+  if (h >= a.num_q_heads) return;
+  const int64_t N = hdr->total_steps;
+  const int64_t weff = hdr->waves;
+  if (N <= 0 || weff <= 0) return;
+  const int* P = reinterpret_cast<const int*>(hdr + 1);
+  const int nch = P[s + 1] - P[s];
+  if (nch <= 0) return;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int kvh = h / G;
+  const int64_t g_item = (int64_t)a.num_kv_heads * P[s] + (int64_t)kvh * nch;
+  const int64_t wf = wave_of_step(g_item, weff, N);
+  const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
+  const int ns = (int)min(wl - wf + 1, (int64_t)a.max_splits);
+  if (ns <= 1) return;
+  const int64_t orow = (int64_t)s * a.num_q_heads + h;
+  const float* ml = a.part_ml + orow * a.max_splits * 2;
+  const float* po = a.part_o + orow * a.max_splits * D;
+  float M = neg_inf();
+  for (int b = lane; b < ns; b += 64) M = fmaxf(M, ml[2 * b]);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
+  float acc[DD];
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) acc[dd] = 0.f;
+  float den = 0.f;
+  for (int b0 = 0; b0 < ns; b0 += 64) {
+    const int b = b0 + lane;
+    const float w = b < ns ? fast_exp2(ml[2 * b] - M) : 0.f;
+    den += b < ns ? w * ml[2 * b + 1] : 0.f;
+    const int nb = min(64, ns - b0);
+    for (int k = 0; k < nb; ++k) {
+      const float wk = __shfl(w, k);
+      const float* p = po + (int64_t)(b0 + k) * D + lane;
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd) acc[dd] += wk * p[64 * dd];
+    }
+  }
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) den += __shfl_xor(den, w);
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) store_elem<ES>(a.out, orow * D + lane + 64 * dd, acc[dd] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -390,10 +693,10 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
   __shared__ float sp[GM][64];
   __shared__ int sid[64];
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
+  const int s = blockIdx.x / a.num_kv_heads;   // (sequence, KV head) fastest: XCD balance
+  const int kvh = blockIdx.x - s * a.num_kv_heads;
   const int j = blockIdx.y;
-  const int s = blockIdx.z / a.num_kv_heads;
-  const int kvh = blockIdx.z - s * a.num_kv_heads;
+  const int split = blockIdx.z;
   const int T = a.num_tokens;
   int r0, qn;
   seq_rows(a.query_start_loc, s, T, r0, qn);
@@ -502,13 +805,19 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge of split partials: out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
-// One workgroup per query token; each wave takes every fourth head.
+// One wave per (query token, head); lanes first read the splits' (m, l)
+// pairs in parallel, then own head_dim columns while summing the weighted
+// partial outputs.
 // ---------------------------------------------------------------------------
 template <int ES, int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   constexpr int DD = D / 64;
-  const int j = blockIdx.x;
-  const int s = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + wave;
+  const int j = blockIdx.y;
+  const int s = blockIdx.z;
+  if (h >= a.num_q_heads) return;
   int r0, qn;
   seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
   if (j >= qn) return;
@@ -518,28 +827,35 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   if (kl <= 0) return;
   const int ns = min((kl + a.split_tokens - 1) / a.split_tokens, a.max_splits);
   if (ns <= 1) return;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  for (int h = wave; h < a.num_q_heads; h += 4) {
-    const int64_t orow = (int64_t)(r0 + j) * a.num_q_heads + h;
-    const float* ml = a.part_ml + orow * a.max_splits * 2;
-    float M = neg_inf();
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, ml[2 * sp]);
-    float acc[DD];
+  const int64_t orow = (int64_t)(r0 + j) * a.num_q_heads + h;
+  const float* ml = a.part_ml + orow * a.max_splits * 2;
+  const float* po = a.part_o + orow * a.max_splits * D;
+  float acc[DD];
 #pragma unroll
-    for (int dd = 0; dd < DD; ++dd) acc[dd] = 0.f;
-    float den = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float w = fast_exp2(ml[2 * sp] - M);
-      den += w * ml[2 * sp + 1];
-      const float* po = a.part_o + (orow * a.max_splits + sp) * D;
+  for (int dd = 0; dd < DD; ++dd) acc[dd] = 0.f;
+  float M = neg_inf();
+  for (int b = lane; b < ns; b += 64) M = fmaxf(M, ml[2 * b]);
 #pragma unroll
-      for (int dd = 0; dd < DD; ++dd) acc[dd] += w * po[lane + 64 * dd];
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
+  float den = 0.f;
+  for (int b0 = 0; b0 < ns; b0 += 64) {
+    const int b = b0 + lane;
+    const float w = b < ns ? fast_exp2(ml[2 * b] - M) : 0.f;
+    den += b < ns ? w * ml[2 * b + 1] : 0.f;
+    const int nb = min(64, ns - b0);
+#pragma unroll 4
+    for (int k = 0; k < nb; ++k) {
+      const float wk = __shfl(w, k);
+      const float* p = po + (int64_t)(b0 + k) * D + lane;
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd) acc[dd] += wk * p[64 * dd];
     }
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int dd = 0; dd < DD; ++dd) store_elem<ES>(a.out, orow * D + lane + 64 * dd, acc[dd] * inv);
   }
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) den += __shfl_xor(den, w);
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) store_elem<ES>(a.out, orow * D + lane + 64 * dd, acc[dd] * inv);
 }
 
 template <int D>
@@ -548,12 +864,12 @@ hipError_t launch_mfma(const AttnArgs& a, bool has_chunks, hipStream_t st) {
   const unsigned z = (unsigned)a.num_seqs * a.num_kv_heads;
   const unsigned narrow_tiles = (unsigned)((G + 15) / 16);
   if (has_chunks) {
-    constexpr int R = 4;
+    constexpr int R = 2;
     const unsigned tiles = (unsigned)(((int64_t)a.max_query_len * G + 16 * R - 1) / (16 * R));
-    attn_mfma_kernel<D, R><<<dim3(a.max_splits, tiles, z), 64, 0, st>>>(a, kMultiRowSeqs);
-    attn_mfma_kernel<D, 1><<<dim3(a.max_splits, narrow_tiles, z), 64, 0, st>>>(a, kSingleRowSeqs);
+    attn_mfma_kernel<D, R><<<dim3(z, tiles, a.max_splits), 64, 0, st>>>(a, kMultiRowSeqs);
+    attn_mfma_kernel<D, 1><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a, kSingleRowSeqs);
   } else {
-    attn_mfma_kernel<D, 1><<<dim3(a.max_splits, narrow_tiles, z), 64, 0, st>>>(a, kAllSeqs);
+    attn_mfma_kernel<D, 1><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a, kAllSeqs);
   }
   return hipGetLastError();
 }
@@ -561,17 +877,49 @@ hipError_t launch_mfma(const AttnArgs& a, bool has_chunks, hipStream_t st) {
 template <int ES, int D>
 hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   const unsigned z = (unsigned)a.num_seqs * a.num_kv_heads;
-  attn_valu_kernel<ES, D><<<dim3(a.max_splits, a.max_query_len, z), 64, 0, st>>>(a);
+  attn_valu_kernel<ES, D><<<dim3(z, a.max_query_len, a.max_splits), 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <int ES, int D>
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
-  merge_kernel<ES, D><<<dim3(a.max_query_len, a.num_seqs), 256, 0, st>>>(a);
+  merge_kernel<ES, D><<<dim3((a.num_q_heads + 3) / 4, a.max_query_len, a.num_seqs), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
+  const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+  // Resident waves: CU count times this kernel's occupancy at this LDS size
+  // (cached for the last device / sequence count seen).
+  static thread_local int c_dev = -1, c_seqs = -1, c_waves = 0;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev != c_dev || a.num_seqs != c_seqs) {
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_streamk_kernel<D>, 64, lds);
+    if (err != hipSuccess) return err;
+    c_dev = dev;
+    c_seqs = a.num_seqs;
+    c_waves = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
+  decode_streamk_kernel<D><<<c_waves, 64, lds, st>>>(a, c_waves, hdr);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  merge_streamk_kernel<2, D><<<dim3((a.num_q_heads + 3) / 4, a.num_seqs), 256, 0, st>>>(a, hdr);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_decode_streamk(const AttnArgs& a, void* header, hipStream_t stream) {
+  return a.head_dim == 128 ? launch_streamk<128>(a, header, stream)
+                           : launch_streamk<64>(a, header, stream);
+}
 
 bool mfma_path(const AttnArgs& a) {
   return a.bf16 && a.block_size >= 8 && (a.head_dim == 64 || a.head_dim == 128);

@@ -58,6 +58,10 @@ EDGE = [
     ("bf16", 16, 1, 64, 32, [300, 260], [100, 3]),               # G = 16 chunks
     ("f32", 8, 2, 64, 4, [50, 12, 64], [20, 12, 1]),             # fp32 chunks
     ("bf16", 8, 2, 128, 4, [50, 12], [20, 1]),                   # bf16 chunks, B = 4
+    ("bf16", 8, 1, 128, 16, [1] * 300, None),                    # many one-token sequences
+    ("bf16", 64, 8, 128, 16, [32768], None),                     # one long context, many pieces
+    ("bf16", 32, 8, 128, 16, [5, 9000, 3, 1, 17000], None),      # ragged mix
+    ("bf16", 32, 8, 64, 32, [4000, 70, 2500], None),             # head_dim 64, B = 32
 ]
 
 
