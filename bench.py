@@ -111,6 +111,7 @@ def main():
     t = wl.tensors
     bt = wl.block_tables_tensor(dev)
     lens = wl.seq_lens_tensor(dev)
+    refcounts = wl.block_refcounts_tensor(dev)
     S, Hq, D = t["query"].shape
     ws = torch.empty(binding.decode_workspace_bytes(S, Hq, D, wl.max_seq_len, shp.block_size,
                                                     args.kv_split), dtype=torch.uint8, device=dev)
@@ -124,7 +125,8 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len, wl.scale,
-                       kv_split_tokens=args.kv_split, out=out, workspace=ws)
+                       kv_split_tokens=args.kv_split, block_refcounts=refcounts, out=out,
+                       workspace=ws)
         if ev is not None:
             ev[1].record(stream)
 

@@ -135,13 +135,21 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * "Physical Block Mapping and Kernel Invocation".
  *   out[s][h] = softmax_t(scale * query[s][h] . K_s[t][h/G]) . V_s[t][h/G],
  *   t = 0 .. seq_lens[s]-1, K_s/V_s gathered through block_tables[s].
+ * block_refcounts (may be NULL) is int32 [num_blocks]: how many block tables
+ * hold each physical block, the reference count of the block manager
+ * ("High-Throughput Local LLM Infrastructure ...", section "1.2", reference
+ * counting and copy-on-write).  It is a cache hint only: blocks with a count
+ * above 1 (shared prefixes) are read through the caches so that every
+ * sharer hits them; all other blocks are streamed with non-temporal loads.
+ * NULL treats every block as private.  Results do not depend on it.
  * max_seq_len must be >= every seq_len.  Keys of one row may be cut into
  * pieces (see pa_decode_workspace_bytes); their partial results are merged
  * exactly (log-sum-exp) in a second pass.
  */
 int pa_decode(void* out, const void* query, const void* k_cache,
               const void* v_cache, const int32_t* block_tables,
-              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+              int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+              const int32_t* seq_lens,
               int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int32_t num_blocks, float scale, int32_t dtype,
@@ -166,10 +174,13 @@ size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
  * P = seq_lens[s] - q_len_s + j and sees keys 0..P.  Sequences with
  * q_len == 1 are decode rows and may be mixed in freely.
  * max_query_len must be >= every q_len and num_tokens == qsl[num_seqs].
+ * block_refcounts: as for pa_decode.
  */
 int pa_chunked_prefill(void* out, const void* query, const void* k_cache,
                        const void* v_cache, const int32_t* block_tables,
-                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                       int32_t max_blocks_per_seq,
+                       const int32_t* block_refcounts,
+                       const int32_t* seq_lens,
                        const int32_t* query_start_loc, int32_t num_seqs,
                        int32_t num_tokens, int32_t max_seq_len,
                        int32_t max_query_len, int32_t num_q_heads,

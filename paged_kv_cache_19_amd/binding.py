@@ -33,12 +33,12 @@ SIGNATURES = {
     "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _vp]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
-                                 _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "pa_chunked_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_chunked_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
-                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
-                                          _i32, _vp, _sz, _vp]),
+    "pa_chunked_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                          _i32, _i32, _vp, _sz, _vp]),
 }
 
 
@@ -147,7 +147,7 @@ def chunked_prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, head_dim,
 
 def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
-           kv_split_tokens: int = 0,
+           kv_split_tokens: int = 0, block_refcounts: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
     S, Hq, D = query.shape
@@ -159,7 +159,8 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 dtype=torch.uint8, device=query.device)
     _check("pa_decode", lib().pa_decode(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-        block_tables.shape[1], _ptr(seq_lens), S, max_seq_len, Hq, Hkv, D, B, NB, scale,
+        block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S, max_seq_len, Hq, Hkv,
+        D, B, NB, scale,
         _dtype(query), kv_split_tokens, _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
@@ -167,7 +168,9 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     block_tables: torch.Tensor, seq_lens: torch.Tensor,
                     query_start_loc: torch.Tensor, max_seq_len: int, max_query_len: int,
-                    scale: float, kv_split_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                    scale: float, kv_split_tokens: int = 0,
+                    block_refcounts: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     T, Hq, D = query.shape
     NB, Hkv, B, _ = k_cache.shape
@@ -180,7 +183,8 @@ def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                                 dtype=torch.uint8, device=query.device)
     _check("pa_chunked_prefill", lib().pa_chunked_prefill(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-        block_tables.shape[1], _ptr(seq_lens), _ptr(query_start_loc), S, T, max_seq_len,
+        block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), _ptr(query_start_loc), S,
+        T, max_seq_len,
         max_query_len, Hq, Hkv, D, B, NB, scale, _dtype(query), kv_split_tokens,
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

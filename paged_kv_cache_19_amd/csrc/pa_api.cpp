@@ -140,7 +140,8 @@ int validate_slots(const int64_t* d_slots, int num_tokens, int64_t num_slots, hi
 }
 
 int attention_common(void* out, const void* query, const void* k_cache, const void* v_cache,
-                     const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+                     const int32_t* block_tables, int max_blocks, const int32_t* refcounts,
+                     const int32_t* seq_lens,
                      const int32_t* qsl, int num_seqs, int num_tokens, int max_seq_len,
                      int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int block_size, int num_blocks, float scale, int dtype, int kv_split_tokens,
@@ -177,6 +178,7 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_tables = block_tables;
+  a.block_refcounts = refcounts;
   a.seq_lens = seq_lens;
   a.query_start_loc = qsl;
   a.out = out;
@@ -284,13 +286,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 }
 
 int pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* block_refcounts, const int32_t* seq_lens,
               int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
               int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
               int32_t dtype, int32_t kv_split_tokens, void* workspace, size_t workspace_bytes,
               void* stream) {
   return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                          seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1, num_q_heads,
+                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                           kv_split_tokens, workspace, workspace_bytes, stream);
 }
@@ -308,7 +311,8 @@ size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
 
 int pa_chunked_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
-                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                       const int32_t* block_refcounts, const int32_t* seq_lens,
+                       const int32_t* query_start_loc,
                        int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
                        int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
@@ -316,7 +320,8 @@ int pa_chunked_prefill(void* out, const void* query, const void* k_cache, const 
                        size_t workspace_bytes, void* stream) {
   if (num_seqs > 0 && num_tokens > 0 && !query_start_loc) return PA_ERR_NULL;
   return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                          seq_lens, query_start_loc, num_seqs, num_tokens, max_seq_len,
+                          block_refcounts, seq_lens, query_start_loc, num_seqs, num_tokens,
+                          max_seq_len,
                           max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
                           num_blocks, scale, dtype, kv_split_tokens, workspace,
                           workspace_bytes, stream);

@@ -14,6 +14,7 @@ struct AttnArgs {
   const void* k_cache;      // [NB, Hkv, B, D]
   const void* v_cache;      // [NB, Hkv, D, B]
   const int32_t* block_tables;
+  const int32_t* block_refcounts;  // nullptr: every block private (cache hint only)
   const int32_t* seq_lens;
   const int32_t* query_start_loc;  // nullptr: one row per sequence
   void* out;                // [T, Hq, D]

@@ -49,6 +49,11 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// Streaming load: the line is not expected to be read again soon.
+__device__ __forceinline__ bf16x8 load_bf16x8_nt(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
@@ -275,6 +280,22 @@ __device__ __forceinline__ void load_rows(const AttnArgs& a, const SeqView& v, i
   }
 }
 
+// Keys held by the sequence's leading shared blocks (reference count above
+// 1), rounded down to whole 32-key steps; looks at the first 64 blocks.
+// Shared blocks always form a prefix of a table: forks copy a table prefix
+// and copy-on-write replaces only a sequence's last block.  Used only to
+// choose the cache policy, never for arithmetic.
+__device__ __forceinline__ int leading_shared_keys(const AttnArgs& a, const SeqView& v) {
+  if (a.block_refcounts == nullptr) return 0;
+  const int lane = threadIdx.x & 63;
+  int id = a.block_tables[(int64_t)v.s * a.max_blocks + min(lane, a.max_blocks - 1)];
+  id = clampi(id, 0, a.num_blocks - 1);
+  const bool shared = lane < v.nblk && a.block_refcounts[id] > 1;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(shared);
+  const int n = (~m == 0) ? 64 : __builtin_ctzll(~m);
+  return min(n << a.log2_block, v.kcap) & ~31;
+}
+
 // Stream keys [k_begin, k_end) of one sequence / KV head through the row
 // tiles, 32 keys per step with the next step's K/V loads in flight.
 //   kv_wave: one past the last key any row of the wave sees (keys from here
@@ -293,7 +314,11 @@ __device__ __forceinline__ void load_rows(const AttnArgs& a, const SeqView& v, i
 // Block ids come from a window of 64 logical blocks held one per lane; a
 // step never straddles two windows (a window is 64*B keys, a multiple of
 // 32), and the next window is loaded one window ahead.
-template <int D, int R>
+//
+// Cache policy: with STREAM every K/V load is non-temporal (private blocks
+// are read once per call); without it loads go through the caches (shared
+// prefix blocks, and query chunks whose K/V several waves re-read).
+template <int D, int R, bool STREAM>
 __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int kv_wave, int kv_min,
                                        int k_begin, int k_end, RowState<D, R>& st) {
   constexpr int KK = D / 32;
@@ -333,11 +358,12 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
     const uint16_t* vp = vbase + block_id(pv_) * blk_stride + (int64_t)i * B + (pv_ & (B - 1));
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      f.ka[kk] = load_bf16x8(ka + 32 * kk);
-      f.kb[kk] = load_bf16x8(kb + 32 * kk);
+      f.ka[kk] = STREAM ? load_bf16x8_nt(ka + 32 * kk) : load_bf16x8(ka + 32 * kk);
+      f.kb[kk] = STREAM ? load_bf16x8_nt(kb + 32 * kk) : load_bf16x8(kb + 32 * kk);
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n) f.v[n] = load_bf16x8(vp + (int64_t)16 * n * B);
+    for (int n = 0; n < NT; ++n)
+      f.v[n] = STREAM ? load_bf16x8_nt(vp + (int64_t)16 * n * B) : load_bf16x8(vp + (int64_t)16 * n * B);
   };
 
   auto compute = [&](KVFrag<D>& f, int c) {
@@ -517,7 +543,16 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
   const int k_end = min(k_begin + a.split_tokens, kv_wave);
   RowState<D, R> st;
   load_rows<D, R>(a, v, row0, st);
-  attend<D, R>(a, v, kv_wave, kv_min, k_begin, k_end, st);
+  if (R == 1) {
+    // Single-tile waves (decode rows) are the only readers of their K/V:
+    // stream it, except the leading shared blocks.
+    const int k_sh = k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) : 0;
+    if (k_sh > k_begin) attend<D, R, false>(a, v, kv_wave, kv_min, k_begin, min(k_sh, k_end), st);
+    if (k_end > max(k_begin, k_sh))
+      attend<D, R, true>(a, v, kv_wave, kv_min, max(k_begin, k_sh), k_end, st);
+  } else {
+    attend<D, R, false>(a, v, kv_wave, kv_min, k_begin, k_end, st);
+  }
   // A row whose keys span more than one split leaves a partial in slot
   // ``split`` for the merge pass; the others are final here.
   write_rows<D, R>(a, v, row0, st, false, split, a.split_tokens, k_begin);
@@ -621,7 +656,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int kl = min(v.L, v.kcap);
     RowState<D, 1> st;
     load_rows<D, 1>(a, v, 0, st);
-    attend<D, 1>(a, v, kl, kl, c0 * 32, min(c1 * 32, kl), st);
+    const int k_begin = c0 * 32;
+    const int k_end = min(c1 * 32, kl);
+    const int k_sh = k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) : 0;
+    if (k_sh > k_begin) attend<D, 1, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+    if (k_end > max(k_begin, k_sh)) attend<D, 1, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf));
     g += c1 - c0;
   }

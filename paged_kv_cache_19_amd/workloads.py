@@ -120,6 +120,14 @@ class Workload:
             bt[s, :len(row)] = torch.tensor(row, dtype=torch.int32)
         return bt.to(device or self.device)
 
+    def block_refcounts_tensor(self, device=None) -> torch.Tensor:
+        """int32 [num_blocks]: how many block tables hold each physical block
+        (the block manager's reference count; 0 for spare blocks)."""
+        rc = torch.zeros(self.num_blocks, dtype=torch.int32)
+        for row in self.block_tables:
+            rc[torch.tensor(row, dtype=torch.long)] += 1
+        return rc.to(device or self.device)
+
     def seq_lens_tensor(self, device=None) -> torch.Tensor:
         return torch.tensor(self.seq_lens, dtype=torch.int32,
                             device=device or self.device)

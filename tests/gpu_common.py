@@ -77,7 +77,7 @@ def sample_rows(wl: workloads.Workload, max_seqs: Optional[int], seed: int = 0) 
 
 def run_and_compare(wl: workloads.Workload, kv_split_tokens: int = 0,
                     max_seqs: Optional[int] = None, do_poison: bool = True,
-                    force_chunked: bool = False):
+                    force_chunked: bool = False, refcounts: bool = True):
     """Full hot path on the GPU (slot mapping, cache write, attention) and the
     oracle on copies of the same inputs.  Returns (out_gpu, max_abs_err)."""
     shp = wl.shape
@@ -104,13 +104,15 @@ def run_and_compare(wl: workloads.Workload, kv_split_tokens: int = 0,
     assert torch.equal(bits(t["k_cache"].cpu()), bits(kc_ref)), "K cache differs"
     assert torch.equal(bits(t["v_cache"].cpu()), bits(vc_ref)), "V cache differs"
 
+    rc = wl.block_refcounts_tensor(dev) if refcounts else None
     if decode_only:
         out = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens,
-                             wl.max_seq_len, wl.scale, kv_split_tokens=kv_split_tokens)
+                             wl.max_seq_len, wl.scale, kv_split_tokens=kv_split_tokens,
+                             block_refcounts=rc)
     else:
         out = binding.chunked_prefill(t["query"], t["k_cache"], t["v_cache"], bt, lens, qsl,
                                       wl.max_seq_len, wl.max_query_len, wl.scale,
-                                      kv_split_tokens=kv_split_tokens)
+                                      kv_split_tokens=kv_split_tokens, block_refcounts=rc)
     torch.cuda.synchronize()
     out_cpu = out.cpu()
     assert torch.isfinite(out_cpu.float()).all(), "non-finite output (poison reached out?)"

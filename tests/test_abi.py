@@ -63,7 +63,7 @@ def _decode(lib, **kw):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, maxb=4, lens=FAKE, S=2, maxlen=64,
              Hq=8, Hkv=2, D=128, B=16, NB=8, scale=0.1, dtype=1, split=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["lens"],
+    return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], None, a["lens"],
                          a["S"], a["maxlen"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
                          a["scale"], a["dtype"], a["split"], a["ws"], a["wsb"], None)
 
@@ -99,11 +99,11 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert rc(None, None, None, None, None, 0, 2, 128, 16, 8, 1, None) == 0
     # chunked prefill: query_start_loc is required
     cp = lib.pa_chunked_prefill
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, 2, 10, 64, 8, 8, 2, 128, 16, 8, 0.1, 1,
-            0, FAKE, 1 << 30, None]
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, FAKE, None, 2, 10, 64, 8, 8, 2, 128, 16, 8, 0.1,
+            1, 0, FAKE, 1 << 30, None]
     assert cp(*args) == -1
-    args[7] = FAKE
-    args[20] = None
+    args[8] = FAKE
+    args[21] = None
     assert cp(*args) == -5
 
 

@@ -76,6 +76,25 @@ def test_edge_shapes(case):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_refcount_hint_changes_nothing(cfg):
+    """The reference counts steer only the cache policy: outputs with and
+    without them are bit-identical."""
+    wl = workloads.make_workload(cfg, device="cuda")
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    lens = wl.seq_lens_tensor("cuda")
+    rc = wl.block_refcounts_tensor("cuda")
+    if cfg == 4:
+        assert int(rc.max()) == wl.num_seqs
+    a = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len, wl.scale)
+    b = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len, wl.scale,
+                       block_refcounts=rc)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16) if a.element_size() == 2 else a.view(torch.int32),
+                       b.view(torch.int16) if b.element_size() == 2 else b.view(torch.int32))
+
+
 def test_decode_through_chunked_entry_point():
     """q_len = 1 rows give the same result through pa_chunked_prefill."""
     wl = workloads.make_workload(2, device="cuda", seq_lens=[300, 1, 4096, 17], q_lens=[1] * 4)
