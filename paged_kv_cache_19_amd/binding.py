@@ -155,7 +155,8 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out is None:
         out = torch.empty_like(query)
     if workspace is None:
-        workspace = torch.empty(decode_workspace_bytes(S, Hq, D, max_seq_len, B, kv_split_tokens),
+        # zero-filled: the balanced decode keeps piece counters in it
+        workspace = torch.zeros(decode_workspace_bytes(S, Hq, D, max_seq_len, B, kv_split_tokens),
                                 dtype=torch.uint8, device=query.device)
     _check("pa_decode", lib().pa_decode(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -178,7 +179,7 @@ def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     if out is None:
         out = torch.empty_like(query)
     if workspace is None:
-        workspace = torch.empty(chunked_prefill_workspace_bytes(S, T, Hq, D, max_seq_len, B,
+        workspace = torch.zeros(chunked_prefill_workspace_bytes(S, T, Hq, D, max_seq_len, B,
                                                                 kv_split_tokens),
                                 dtype=torch.uint8, device=query.device)
     _check("pa_chunked_prefill", lib().pa_chunked_prefill(

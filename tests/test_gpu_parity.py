@@ -95,6 +95,26 @@ def test_refcount_hint_changes_nothing(cfg):
                        b.view(torch.int16) if b.element_size() == 2 else b.view(torch.int32))
 
 
+def test_workspace_reuse():
+    """Consecutive calls on one workspace match calls on fresh workspaces bit
+    for bit (nothing in the workspace carries over between calls)."""
+    wl = workloads.make_workload(3, device="cuda", seq_lens=[8000, 3000, 20000, 77, 4096],
+                                 q_lens=[1] * 5)
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    S, Hq, D = t["query"].shape
+    B = wl.shape.block_size
+    ws = torch.full((binding.decode_workspace_bytes(S, Hq, D, 20000, B),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    for lens in ([8000, 3000, 20000, 77, 4096], [100, 3000, 19000, 77, 1], [8000, 3000, 20000, 77, 4096]):
+        lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        got = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lt, 20000, wl.scale,
+                             workspace=ws)
+        ref = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lt, 20000, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 def test_decode_through_chunked_entry_point():
     """q_len = 1 rows give the same result through pa_chunked_prefill."""
     wl = workloads.make_workload(2, device="cuda", seq_lens=[300, 1, 4096, 17], q_lens=[1] * 4)
