@@ -142,6 +142,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * above 1 (shared prefixes) are read through the caches so that every
  * sharer hits them; all other blocks are streamed with non-temporal loads.
  * NULL treats every block as private.  Results do not depend on it.
+ * scale must be finite and > 0 (1/sqrt(head_dim) in the pages); other
+ * values return PA_ERR_SHAPE.
  * max_seq_len must be >= every seq_len.  Keys of one row may be cut into
  * pieces (see pa_decode_workspace_bytes); their partial results are merged
  * exactly (log-sum-exp) in a second pass.
@@ -156,7 +158,13 @@ int pa_decode(void* out, const void* query, const void* k_cache,
               int32_t kv_split_tokens, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* Workspace for pa_chunked_prefill (same meaning as for pa_decode). */
+/*
+ * Workspace for pa_chunked_prefill: fp32 partials for the query-chunk rows
+ * (num_tokens * num_q_heads rows, one slot per kv_split_tokens keys, 2048
+ * when 0), fp32 pieces for the balanced decode of single-token rows
+ * (num_seqs * num_q_heads rows) and a small header.  Returns 0 for invalid
+ * arguments.
+ */
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
                                           int32_t num_q_heads,
                                           int32_t head_dim,
@@ -174,7 +182,8 @@ size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
  * P = seq_lens[s] - q_len_s + j and sees keys 0..P.  Sequences with
  * q_len == 1 are decode rows and may be mixed in freely.
  * max_query_len must be >= every q_len and num_tokens == qsl[num_seqs].
- * block_refcounts: as for pa_decode.
+ * block_refcounts and scale: as for pa_decode.  On the bf16 path at most
+ * 2048 sequences per call (PA_ERR_UNSUPPORTED above that).
  */
 int pa_chunked_prefill(void* out, const void* query, const void* k_cache,
                        const void* v_cache, const int32_t* block_tables,

@@ -14,7 +14,8 @@
 
 namespace {
 
-constexpr int kDefaultSplitTokens = 512;
+constexpr int kDefaultSplitTokens = 512;        // decode rows on the fixed-split path
+constexpr int kDefaultChunkSplitTokens = 2048;  // query-chunk rows
 // The balanced decode keeps every sequence's step prefix sum in LDS.
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kAlign = 256;
@@ -28,11 +29,10 @@ bool check_enabled() {
   return v && v[0] && strcmp(v, "0") != 0;
 }
 
-// Keys one split covers on the fixed-split path: 0 selects the default,
+// Keys one split covers on the fixed-split paths: 0 selects the default,
 // otherwise a positive multiple of 64.
-int split_tokens_for(int requested, int block_size) {
-  (void)block_size;
-  if (requested == 0) return kDefaultSplitTokens;
+int split_tokens_for(int requested, bool chunks) {
+  if (requested == 0) return chunks ? kDefaultChunkSplitTokens : kDefaultSplitTokens;
   if (requested < 0 || requested % 64 != 0) return -1;
   return requested;
 }
@@ -49,41 +49,48 @@ int check_common(int num_q_heads, int num_kv_heads, int head_dim, int block_size
 }
 
 struct WorkspacePlan {
-  int split_tokens = 0;   // fixed-split path: keys per split
-  int max_splits = 0;     // fixed-split path: partial slots per row
+  int split_tokens = 0;   // fixed-split / chunk path: keys per split
+  int max_splits = 0;     // fixed-split / chunk path: partial slots per row
   int max_pieces = 0;     // balanced decode: partial slots per row (0: unused)
-  int slots = 0;          // partial slots per row reserved in the workspace
-  size_t part_o_bytes = 0;
-  size_t part_ml_bytes = 0;
-  size_t header_bytes = 0;
+  size_t a_o = 0, a_ml = 0;  // region A: [T*Hq, max_splits] partials (o, then (m, l))
+  size_t b_o = 0, b_ml = 0;  // region B: [S*Hq, max_pieces] balanced-decode pieces
+  size_t header = 0;         // balanced-decode header
   size_t total = 0;
 };
 
-// Workspace layout: part_o [rows, slots, D] fp32 | part_ml [rows, slots, 2]
-// fp32 | balanced-decode header (step total, wave count, per-sequence step
-// prefix sums).  rows = query tokens * query heads.
-bool plan_workspace(int num_rows_tokens, int num_seqs, int num_q_heads, int head_dim,
-                    int max_seq_len, int block_size, int kv_split_tokens, bool balanced_decode,
-                    WorkspacePlan* p) {
-  if (num_rows_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 ||
+// Workspace layout: region A (fixed-split and query-chunk partials, one row
+// per query token and head) | region B (balanced-decode pieces, one row per
+// sequence and head) | header (step total, wave count, per-sequence step
+// prefix sums).  pa_decode's two paths share one region (rows = sequences),
+// so its size is the larger of the two slot counts.
+bool plan_workspace(int num_tokens, int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
+                    int block_size, int kv_split_tokens, bool chunk_entry, WorkspacePlan* p) {
+  if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 ||
       max_seq_len <= 0 || !is_pow2(block_size) || block_size > 64)
     return false;
-  const int st = split_tokens_for(kv_split_tokens, block_size);
+  const int st = split_tokens_for(kv_split_tokens, chunk_entry);
   if (st <= 0) return false;
   p->split_tokens = st;
   p->max_splits = (max_seq_len + st - 1) / st;
-  p->max_pieces = 0;
-  if (balanced_decode && kv_split_tokens == 0) {
-    const int steps = (max_seq_len + 31) / 32;
-    p->max_pieces = (steps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
+  const int steps = (max_seq_len + 31) / 32;
+  p->max_pieces = (steps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
+  const size_t ob = (size_t)head_dim * sizeof(float), mlb = 2 * sizeof(float);
+  if (chunk_entry) {
+    const size_t ra = (size_t)num_tokens * num_q_heads * p->max_splits;
+    const size_t rb = (size_t)num_seqs * num_q_heads * p->max_pieces;
+    p->a_o = align_up(ra * ob);
+    p->a_ml = align_up(ra * mlb);
+    p->b_o = align_up(rb * ob);
+    p->b_ml = align_up(rb * mlb);
+  } else {
+    if (kv_split_tokens != 0) p->max_pieces = 0;
+    const int slots = p->max_splits > p->max_pieces ? p->max_splits : p->max_pieces;
+    const size_t r = (size_t)num_seqs * num_q_heads * slots;
+    p->a_o = align_up(r * ob);
+    p->a_ml = align_up(r * mlb);
   }
-  p->slots = p->max_splits > p->max_pieces ? p->max_splits : p->max_pieces;
-  const size_t rows = (size_t)num_rows_tokens * num_q_heads * p->slots;
-  p->part_o_bytes = align_up(rows * head_dim * sizeof(float));
-  p->part_ml_bytes = align_up(rows * 2 * sizeof(float));
-  p->header_bytes = p->max_pieces ? align_up(16 + (size_t)(num_seqs + 1) * 4) : 0;
-  p->total = p->part_o_bytes + p->part_ml_bytes + p->header_bytes;
-  if (p->total == 0) p->total = kAlign;
+  p->header = align_up(16 + (size_t)(num_seqs + 1) * 4);
+  p->total = p->a_o + p->a_ml + p->b_o + p->b_ml + p->header;
   return true;
 }
 
@@ -149,14 +156,15 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
   if (num_seqs < 0 || num_tokens < 0 || max_blocks <= 0 || num_blocks <= 0 ||
-      max_seq_len <= 0 || max_query_len <= 0 || !isfinite(scale))
+      max_seq_len <= 0 || max_query_len <= 0 || !isfinite(scale) || !(scale > 0.f))
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
   if ((int64_t)num_seqs * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   WorkspacePlan plan;
+  const bool chunk_entry = qsl != nullptr;
   if (!plan_workspace(num_tokens, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, qsl == nullptr, &plan))
+                      kv_split_tokens, chunk_entry, &plan))
     return PA_ERR_SHAPE;
   if (plan.max_splits > 65535) return PA_ERR_UNSUPPORTED;
   if (!workspace) return PA_ERR_WORKSPACE;
@@ -164,16 +172,20 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   pa::AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.bf16 = dtype == PA_BF16;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  const bool mfma = pa::mfma_path(a);
   const int G = num_q_heads / num_kv_heads;
-  const bool mfma = a.bf16 && block_size >= 8;
-  const int64_t tiles_y = mfma ? ((int64_t)max_query_len * G + 63) / 64 : max_query_len;
-  if (tiles_y > 65535) return PA_ERR_UNSUPPORTED;
+  if (mfma && chunk_entry && num_seqs > pa::kMaxChunkSeqs) return PA_ERR_UNSUPPORTED;
+  const int64_t tiles_y = mfma ? ((int64_t)G + 15) / 16 : max_query_len;
+  if (tiles_y > 65535 || (int64_t)num_tokens > 65535 * 64) return PA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (check_enabled()) {
     rc = validate_metadata(block_tables, max_blocks, seq_lens, qsl, num_seqs, num_tokens,
                            max_seq_len, max_query_len, block_size, num_blocks, st);
     if (rc != PA_OK) return rc;
   }
+  char* ws = static_cast<char*>(workspace);
   a.q = query;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -182,28 +194,33 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   a.seq_lens = seq_lens;
   a.query_start_loc = qsl;
   a.out = out;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_o_bytes);
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + plan.a_o);
   a.max_blocks = max_blocks;
   a.num_seqs = num_seqs;
   a.num_tokens = num_tokens;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.block_size = block_size;
   a.log2_block = log2i(block_size);
   a.num_blocks = num_blocks;
   a.split_tokens = plan.split_tokens;
+  a.max_splits = plan.max_splits;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * 1.4426950408889634f;
+  void* header = ws + plan.a_o + plan.a_ml + plan.b_o + plan.b_ml;
   hipError_t err;
-  if (plan.max_pieces > 0 && pa::mfma_path(a) && num_seqs <= kMaxBalancedSeqs) {
-    a.max_splits = plan.max_pieces;
-    err = pa::launch_decode_streamk(
-        a, static_cast<char*>(workspace) + plan.part_o_bytes + plan.part_ml_bytes, st);
+  if (chunk_entry) {
+    a.sk_part_o = reinterpret_cast<float*>(ws + plan.a_o + plan.a_ml);
+    a.sk_part_ml = reinterpret_cast<float*>(ws + plan.a_o + plan.a_ml + plan.b_o);
+    a.sk_slots = plan.max_pieces;
+    err = pa::launch_attention(a, true, header, st);
+  } else if (plan.max_pieces > 0 && mfma && num_seqs <= kMaxBalancedSeqs) {
+    a.sk_part_o = a.part_o;   // pa_decode: one region, rows = sequences
+    a.sk_part_ml = a.part_ml;
+    a.sk_slots = plan.max_pieces;
+    err = pa::launch_decode_streamk(a, header, st);
   } else {
-    a.max_splits = plan.max_splits;
-    err = pa::launch_attention(a, qsl != nullptr && max_query_len > 1, st);
+    err = pa::launch_attention(a, false, nullptr, st);
   }
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -280,7 +297,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t kv_split_tokens) {
   WorkspacePlan p;
   if (!plan_workspace(num_seqs, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, true, &p))
+                      kv_split_tokens, false, &p))
     return 0;
   return p.total;
 }
@@ -304,7 +321,7 @@ size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
                                           int32_t kv_split_tokens) {
   WorkspacePlan p;
   if (!plan_workspace(num_tokens, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, false, &p))
+                      kv_split_tokens, true, &p))
     return 0;
   return p.total;
 }

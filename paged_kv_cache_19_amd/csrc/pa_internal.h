@@ -18,12 +18,15 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* query_start_loc;  // nullptr: one row per sequence
   void* out;                // [T, Hq, D]
-  float* part_o;            // [T * Hq, max_splits, D]
-  float* part_ml;           // [T * Hq, max_splits, 2]  (max in log2 units, sum)
+  float* part_o;            // [T * Hq, max_splits, D]   fixed-split / chunk partials
+  float* part_ml;           // [T * Hq, max_splits, 2]   (max in log2 units, sum)
+  float* sk_part_o;         // [num_seqs * Hq, sk_slots, D] balanced-decode pieces
+  float* sk_part_ml;        // [num_seqs * Hq, sk_slots, 2]
   int32_t max_blocks;
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
   int32_t block_size, log2_block, num_blocks;
   int32_t split_tokens, max_splits, max_query_len;
+  int32_t sk_slots;         // pieces per row in sk_part_*
   float scale_log2;         // scale * log2(e)
   int32_t bf16;             // 1: bf16 elements, 0: fp32
 };
@@ -50,7 +53,15 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 
 // Split-K attention pass (writes final rows for single-split rows and
 // partials otherwise), then the log-sum-exp merge pass when needed.
-hipError_t launch_attention(const AttnArgs& a, bool has_chunks, hipStream_t stream);
+// ``has_chunks``: rows of multi-token sequences go to the persistent chunk
+// kernel and single-token rows to the balanced decode (whose ``header`` is
+// workspace as for launch_decode_streamk).
+hipError_t launch_attention(const AttnArgs& a, bool has_chunks, void* header,
+                            hipStream_t stream);
+
+// Largest batch the persistent chunk kernel takes (its per-sequence item
+// prefix sums live in LDS).
+constexpr int kMaxChunkSeqs = 2048;
 
 // Balanced ("stream-K") decode over a fixed set of resident waves, then the
 // merge of the pieces.  ``header`` is workspace for the step prefix sums

@@ -449,6 +449,15 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
   }
 }
 
+// Where a wave's partial (o, m, l) rows go: ``slots`` partials per row,
+// row index = row_base + head when row_base >= 0, else the output row.
+struct PartialDst {
+  float* o;
+  float* ml;
+  int slots;
+  int64_t row_base;
+};
+
 // Write the wave's rows: normalised output when ``whole`` (this piece saw
 // every key of the row), else the piece's (o, m, l) into partial slot
 // ``slot`` of the row.  Lane l holds rows 4*(l/16)+r, columns 16*n + l%16.
@@ -459,7 +468,8 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
 template <int D, int R>
 __device__ __forceinline__ void write_rows(const AttnArgs& a, const SeqView& v, int row0,
                                            const RowState<D, R>& st, bool whole, int slot,
-                                           int split_tokens = 0, int k_begin = 0) {
+                                           const PartialDst& pd, int split_tokens = 0,
+                                           int k_begin = 0) {
   constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
   const int i = lane & 15;
@@ -486,21 +496,22 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const SeqView& v, 
       if (split_tokens > 0) {
         const int kl = min(v.L - v.qn + j + 1, v.kcap);
         if (kl <= k_begin) continue;
-        final_row = min((kl + split_tokens - 1) / split_tokens, a.max_splits) == 1;
+        final_row = min((kl + split_tokens - 1) / split_tokens, pd.slots) == 1;
       }
       if (final_row) {
         const float inv = 1.f / lr[r];
 #pragma unroll
         for (int n = 0; n < NT; ++n) out[orow * D + 16 * n + i] = f32_to_bf16_bits(st.o[t][n][r] * inv);
       } else {
-        if (slot >= a.max_splits) continue;  // out-of-contract lengths: stay in bounds
-        const int64_t pidx = orow * a.max_splits + slot;
-        float* po = a.part_o + pidx * D;
+        if (slot >= pd.slots) continue;  // out-of-contract lengths: stay in bounds
+        const int64_t prow = pd.row_base >= 0 ? pd.row_base + v.kvh * G + g : orow;
+        const int64_t pidx = prow * pd.slots + slot;
+        float* po = pd.o + pidx * D;
 #pragma unroll
         for (int n = 0; n < NT; ++n) po[16 * n + i] = st.o[t][n][r];
         if (i == 0) {
-          a.part_ml[2 * pidx] = mr[r];
-          a.part_ml[2 * pidx + 1] = lr[r];
+          pd.ml[2 * pidx] = mr[r];
+          pd.ml[2 * pidx + 1] = lr[r];
         }
       }
     }
@@ -555,7 +566,8 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
   }
   // A row whose keys span more than one split leaves a partial in slot
   // ``split`` for the merge pass; the others are final here.
-  write_rows<D, R>(a, v, row0, st, false, split, a.split_tokens, k_begin);
+  write_rows<D, R>(a, v, row0, st, false, split, PartialDst{a.part_o, a.part_ml, a.max_splits, -1},
+                   a.split_tokens, k_begin);
 }
 
 // ---------------------------------------------------------------------------
@@ -592,8 +604,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int lg = a.log2_block;
   for (int s = lane; s < S; s += 64) {
     const int L = a.seq_lens[s];
+    int r0, qn;
+    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
     const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
-    P[s + 1] = kl > 0 ? (kl + 31) >> 5 : 0;
+    // Only single-token rows are decode work (query chunks have their own kernel).
+    P[s + 1] = (qn == 1 && kl > 0) ? (kl + 31) >> 5 : 0;
     Ls[s] = L;
   }
   __syncthreads();
@@ -652,7 +667,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int64_t g_item = base + (int64_t)kvh * nch;
     const int64_t wf = wave_of_step(g_item, weff, N);
     const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
-    const SeqView v = seq_view(a, s, kvh, Ls[s], s, 1);
+    int r0, qn;
+    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+    const SeqView v = seq_view(a, s, kvh, Ls[s], r0, 1);
     const int kl = min(v.L, v.kcap);
     RowState<D, 1> st;
     load_rows<D, 1>(a, v, 0, st);
@@ -661,7 +678,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int k_sh = k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) : 0;
     if (k_sh > k_begin) attend<D, 1, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
     if (k_end > max(k_begin, k_sh)) attend<D, 1, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
-    write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf));
+    write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
+                     PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
     g += c1 - c0;
   }
 }
@@ -687,11 +705,14 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   const int64_t g_item = (int64_t)a.num_kv_heads * P[s] + (int64_t)kvh * nch;
   const int64_t wf = wave_of_step(g_item, weff, N);
   const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
-  const int ns = (int)min(wl - wf + 1, (int64_t)a.max_splits);
+  const int ns = (int)min(wl - wf + 1, (int64_t)a.sk_slots);
   if (ns <= 1) return;
-  const int64_t orow = (int64_t)s * a.num_q_heads + h;
-  const float* ml = a.part_ml + orow * a.max_splits * 2;
-  const float* po = a.part_o + orow * a.max_splits * D;
+  int r0, qn;
+  seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+  const int64_t prow = (int64_t)s * a.num_q_heads + h;
+  const int64_t orow = (int64_t)r0 * a.num_q_heads + h;
+  const float* ml = a.sk_part_ml + prow * a.sk_slots * 2;
+  const float* po = a.sk_part_o + prow * a.sk_slots * D;
   float M = neg_inf();
   for (int b = lane; b < ns; b += 64) M = fmaxf(M, ml[2 * b]);
 #pragma unroll
@@ -717,6 +738,316 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   const float inv = 1.f / den;
 #pragma unroll
   for (int dd = 0; dd < DD; ++dd) store_elem<ES>(a.out, orow * D + lane + 64 * dd, acc[dd] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Query-chunk attention (chunked prefill) on v_mfma_f32_32x32x16_bf16 with
+// K/V staged in LDS.  One workgroup of 4 waves serves 128 query rows
+// (row = j * G + g) of one (sequence, KV head) and one split of keys; each
+// wave owns 32 rows, so one 32-key step costs every wave 2*D/16 MFMAs against
+// 16*D bytes of K/V that the whole workgroup loads once.
+//
+// S^T = K Q^T (A = K rows of the step, B = Q^T): the accumulator gives lane
+// l the 16 scores of query row l%32 at MFMA rows (r/4)*8 + 4*(l/32) + r%4.
+// Mapping MFMA row m to step token sigma32(m) (quads 1 and 2 of every 16
+// swapped) makes registers 8k..8k+7 of that accumulator hold tokens
+// 16k + 8*(l/32) .. +7 -- exactly the B operand P^T of O^T = V^T P^T for the
+// k-th 16-key MFMA step.  In O^T every register of lane l belongs to query
+// row l%32, so the online-softmax rescale is lane-local.
+//
+// LDS holds two stages of [K tile 32 x D | V^T tile D x 32].  Tiles are
+// written 16 bytes per lane contiguously and read in MFMA operand order;
+// the 16-byte chunks are XOR-swizzled so that both the K reads (32 token
+// rows, one chunk each) and the V^T reads (32 head_dim rows) are free of
+// bank conflicts.  The tiles are filled by direct global->LDS loads
+// (16 bytes per lane, no registers) kPrefillStages-1 steps ahead of the
+// step being computed; each wave waits for its own loads with vmcnt and a
+// workgroup barrier publishes the stage.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPrefillRows = 128;  // query rows per workgroup
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillStages = 4;  // LDS ring of K/V steps
+
+// global_load_lds of 16 bytes: lane l's bytes land at lds_base + 16 * l.
+__device__ __forceinline__ void load_to_lds(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ int sigma32(int m) {
+  const int q = (m >> 2) & 3;
+  const int qq = q == 1 ? 2 : (q == 2 ? 1 : q);
+  return (m & 16) | (qq << 2) | (m & 3);
+}
+
+// Swizzle of the 16-byte chunks of K row t (D/8 chunks per row; rows of
+// 2*D bytes, 128/D rows per 256-byte bank sweep).
+template <int D>
+__device__ __forceinline__ int ksw(int t) {
+  return (t / (128 / D)) % (D / 8);
+}
+
+// Work items of the chunk kernel: (sequence with q_len > 1, split, KV head,
+// row tile), row tile fastest so that the 128-row tiles sharing one
+// (sequence, KV head, split) -- and so one stretch of K/V -- are consecutive.
+// The kernel is persistent: a fixed set of resident workgroups walks the
+// item list in rounds; within a round the workgroups of one XCD take a
+// contiguous run of items (workgroups are dealt to the 8 XCDs round-robin),
+// so tiles that share K/V run together on one XCD and share its L2.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
+    AttnArgs a, int num_wgs) {
+  constexpr int KS = D / 16;                       // S^T MFMA steps over head_dim
+  constexpr int DT = D / 32;                       // O^T head_dim tiles
+  constexpr int CPR = D / 8;                       // 16-byte chunks per K row
+  constexpr int RPI = 1024 / (2 * D);              // K rows per 1 KiB load
+  constexpr int IPW = (D / 16) / kPrefillWaves;    // 1 KiB loads per wave per tile
+  constexpr int NS = kPrefillStages;
+  constexpr int DMA_PER_STEP = 2 * IPW;            // loads per wave per step
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NS][2][32 * D];
+  extern __shared__ int item_prefix[];             // [num_seqs + 1]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  const int S = a.num_seqs;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int lg = a.log2_block;
+  const int B = 1 << lg;
+  const int ST = a.split_tokens;
+
+  // Items per sequence, then their prefix sums (one thread per sequence,
+  // a simple serial scan over 256-sequence segments).
+  for (int s = tid; s < S; s += 256) {
+    int r0, qn;
+    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+    int n = 0;
+    if (qn > 1) {
+      const int L = a.seq_lens[s];
+      const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
+      const int tiles = (qn * G + kPrefillRows - 1) / kPrefillRows;
+      const int splits = min((kl + ST - 1) / ST, a.max_splits);
+      n = kl > 0 ? tiles * a.num_kv_heads * splits : 0;
+    }
+    item_prefix[s + 1] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    item_prefix[0] = 0;
+    for (int s = 0; s < S; ++s) item_prefix[s + 1] += item_prefix[s];
+  }
+  __syncthreads();
+  const int total = item_prefix[S];
+  const int wg = blockIdx.x;
+
+  for (int k = (wg & 7) * (num_wgs >> 3) + (wg >> 3); k < total; k += num_wgs) {
+    // -- decode item k -------------------------------------------------------
+    int s;
+    {
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (item_prefix[mid] <= k) lo = mid;
+        else hi = mid - 1;
+      }
+      s = lo;
+    }
+    int r0, qn;
+    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+    const int nrows = qn * G;
+    const int tiles = (nrows + kPrefillRows - 1) / kPrefillRows;
+    int rem = k - item_prefix[s];
+    const int tile = rem % tiles;
+    rem /= tiles;
+    const int kvh = rem % a.num_kv_heads;
+    const int split = rem / a.num_kv_heads;
+    const int L = a.seq_lens[s];
+    const SeqView v = seq_view(a, s, kvh, L, r0, qn);
+    const int row0 = tile * kPrefillRows;
+    const int row_last = min(row0 + kPrefillRows, nrows) - 1;
+    const int kv_wg = min(L - qn + row_last / G + 1, v.kcap);
+    const int k_begin = split * ST;
+    if (k_begin >= kv_wg) continue;  // workgroup-uniform
+    const int k_end = min(k_begin + ST, kv_wg);
+
+    const int wrow0 = row0 + 32 * w;
+    const bool wave_active = wrow0 < nrows;
+    const int kv_wmin = wave_active ? min(L - qn + wrow0 / G + 1, v.kcap) : 0;
+    const int row = wrow0 + c32;
+    const bool row_ok = row < nrows;
+    const int jrow = row_ok ? row / G : 0;
+    const int grow = row_ok ? row - jrow * G : 0;
+    const int klim = row_ok ? min(L - qn + jrow + 1, v.kcap) : 0;
+
+    bf16x8 qf[KS];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(r0 + jrow) * a.num_q_heads + kvh * G + grow) * D + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? load_bf16x8(qp + 16 * ks) : bf16x8{};
+    }
+
+    const int64_t trow = (int64_t)s * a.max_blocks;
+    // Block ids are clamped into the pool when a window becomes current, not
+    // when it is loaded: the prefetched next window is not waited for early.
+    auto window = [&](int b0) { return a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)]; };
+    int blk0 = k_begin >> lg;
+    int wid = clampi(window(blk0), 0, a.num_blocks - 1);
+    int wid_next = window(blk0 + 64);
+    auto block_id = [&](int pos) { return __shfl(wid, min(pos >> lg, v.nblk - 1) - blk0); };
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * B * D;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * B * D;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D * B;
+
+    // This wave's share of one step: IPW 1 KiB pieces of the K tile and of
+    // the V^T tile, written lane-contiguously into stage ``st``.
+    auto dma = [&](int c, int st) {
+      if ((c >> lg) - blk0 >= 64) {  // wave-uniform: next window of block ids
+        blk0 += 64;
+        wid = clampi(wid_next, 0, a.num_blocks - 1);
+        wid_next = window(blk0 + 64);
+      }
+#pragma unroll
+      for (int x2 = 0; x2 < IPW; ++x2) {
+        const int x = w * IPW + x2;
+        const int t = x * RPI + lane / CPR;
+        const int chunk = (lane % CPR) ^ ksw<D>(t);
+        const int pos = c + t;
+        load_to_lds(kbase + block_id(pos) * blk_stride + (pos & (B - 1)) * D + chunk * 8,
+                    &smem[st][0][x * 512]);
+        const int d = 16 * x + (lane >> 2);
+        const int vc = (lane & 3) ^ ((d >> 2) & 3);
+        const int vpos = c + 8 * vc;
+        load_to_lds(vbase + block_id(vpos) * blk_stride + (int64_t)d * B + (vpos & (B - 1)),
+                    &smem[st][1][x * 512]);
+      }
+    };
+
+    float m = neg_inf(), l = 0.f;
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+    const float sl2 = a.scale_log2;  // > 0 (checked by the host)
+    const int tk = sigma32(c32);
+
+    auto compute = [&](int st, int c) {
+      const uint16_t* kt = smem[st][0];
+      const uint16_t* vt = smem[st][1];
+      f32x16 sacc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(kt + tk * D + (((2 * ks + h) ^ ksw<D>(tk)) * 8));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+      }
+      // Scores stay unscaled until the exponent: max(s * sl2) = max(s) * sl2.
+      float sv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
+      if (c + 32 > kv_wmin) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = sigma32((r >> 2) * 8 + 4 * h + (r & 3));
+          sv[r] = (c + tok < klim) ? sv[r] : neg_inf();
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+      {
+        auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])) * sl2;
+      }
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescaleLog2) != 0) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - ((mnew == neg_inf()) ? 0.f : mnew));
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m = mnew;
+      }
+      const float nm = (m == neg_inf()) ? 0.f : -m;
+      float ps = 0.f;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sv[r], sl2, nm));
+        ps += p;
+        pf[r >> 3][r & 7] = static_cast<__bf16>(p);
+      }
+      {
+        auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+        l += __uint_as_float(q[0]) + __uint_as_float(q[1]);
+      }
+      const bool tail = c + 32 > kv_wg;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + c32;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(vt + d * 32 + (((2 * k2 + h) ^ ((d >> 2) & 3)) * 8));
+          if (tail) {
+            // keys past the last visible one may be unwritten slots
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (c + 16 * k2 + 8 * h + e >= kv_wg) vf[e] = static_cast<__bf16>(0.f);
+          }
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k2], o[dt], 0, 0, 0);
+        }
+      }
+    };
+
+    // Ring of NS stages: step i lives in stage i % NS and is loaded NS-1
+    // iterations ahead.  Iteration i waits for this wave's loads of step i
+    // (the loads of the two younger steps may stay in flight); the barrier
+    // then publishes every wave's loads and also guarantees that all waves
+    // finished step i-1, whose stage the new loads overwrite.  The loads of
+    // steps past the end re-read the last step so that the count of loads
+    // in flight is the same in every iteration.
+    const int nsteps = (k_end - k_begin + 31) >> 5;
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) dma(k_begin + 32 * min(p, nsteps - 1), p);
+    for (int i = 0; i < nsteps; ++i) {
+      __builtin_amdgcn_s_waitcnt(0x3F70 | ((NS - 2) * DMA_PER_STEP));  // vmcnt
+      __builtin_amdgcn_s_barrier();
+      dma(k_begin + 32 * min(i + NS - 1, nsteps - 1), (i + NS - 1) % NS);
+      if (wave_active) compute(i % NS, k_begin + 32 * i);
+    }
+    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): the ring is quiet
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();        // before the next item refills it
+
+    if (row_ok && klim > k_begin) {
+      const int ns = min((klim + ST - 1) / ST, a.max_splits);
+      const int64_t orow = (int64_t)(r0 + jrow) * a.num_q_heads + kvh * G + grow;
+      if (ns == 1) {
+        const float inv = 1.f / l;
+        uint16_t* out = static_cast<uint16_t*>(a.out) + orow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            out[32 * dt + (r >> 2) * 8 + 4 * h + (r & 3)] = f32_to_bf16_bits(o[dt][r] * inv);
+      } else {
+        const int64_t pidx = orow * a.max_splits + split;
+        float* po = a.part_o + pidx * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) po[32 * dt + (r >> 2) * 8 + 4 * h + (r & 3)] = o[dt][r];
+        if (h == 0) {
+          a.part_ml[2 * pidx] = m;
+          a.part_ml[2 * pidx + 1] = l;
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -849,24 +1180,35 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 // partial outputs.
 // ---------------------------------------------------------------------------
 template <int ES, int D>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single) {
   constexpr int DD = D / 64;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.x * 4 + wave;
-  const int j = blockIdx.y;
-  const int s = blockIdx.z;
+  const int t = blockIdx.y;  // query token row
   if (h >= a.num_q_heads) return;
+  int s = t;
+  if (a.query_start_loc) {  // largest s with qsl[s] <= t
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.query_start_loc[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    s = lo;
+  }
   int r0, qn;
   seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-  if (j >= qn) return;
+  const int j = t - r0;
+  if (j < 0 || j >= qn) return;
+  if (skip_single && qn == 1) return;  // merged by the balanced decode's pass
   const int L = a.seq_lens[s];
   const int nblk = table_blocks(L, a.log2_block, a.max_blocks);
   const int kl = min(L - qn + j + 1, nblk << a.log2_block);
   if (kl <= 0) return;
   const int ns = min((kl + a.split_tokens - 1) / a.split_tokens, a.max_splits);
   if (ns <= 1) return;
-  const int64_t orow = (int64_t)(r0 + j) * a.num_q_heads + h;
+  const int64_t orow = (int64_t)t * a.num_q_heads + h;
   const float* ml = a.part_ml + orow * a.max_splits * 2;
   const float* po = a.part_o + orow * a.max_splits * D;
   float acc[DD];
@@ -897,60 +1239,95 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   for (int dd = 0; dd < DD; ++dd) store_elem<ES>(a.out, orow * D + lane + 64 * dd, acc[dd] * inv);
 }
 
+// Resident workgroups of a persistent kernel on the current device: CUs
+// times its occupancy at this LDS size (cached for the last call site,
+// device and sequence count).
+struct Residency {
+  int dev = -1, seqs = -1, n = 0;
+};
+
+template <typename K>
+hipError_t resident(Residency& c, K kernel, int threads, size_t lds, int seqs, int& n) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev != c.dev || seqs != c.seqs) {
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
+    if (err != hipSuccess) return err;
+    c.dev = dev;
+    c.seqs = seqs;
+    c.n = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  n = c.n;
+  return hipSuccess;
+}
+
 template <int D>
-hipError_t launch_mfma(const AttnArgs& a, bool has_chunks, hipStream_t st) {
+hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
+  static thread_local Residency cache;
+  const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+  int waves = 0;
+  hipError_t err = resident(cache, decode_streamk_kernel<D>, 64, lds, a.num_seqs, waves);
+  if (err != hipSuccess) return err;
+  StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
+  decode_streamk_kernel<D><<<waves, 64, lds, st>>>(a, waves, hdr);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  merge_streamk_kernel<2, D><<<dim3((a.num_q_heads + 3) / 4, a.num_seqs), 256, 0, st>>>(a, hdr);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t st) {
+  static thread_local Residency cache;
+  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+  int n = 0;
+  hipError_t err = resident(cache, prefill_kernel<D>, 256, lds, a.num_seqs, n);
+  if (err != hipSuccess) return err;
+  n = n >= 8 ? n / 8 * 8 : 8;  // the item walk deals runs of items to the 8 XCDs
+  prefill_kernel<D><<<n, 256, lds, st>>>(a, n);
+  return hipGetLastError();
+}
+
+template <int ES, int D>
+hipError_t launch_merge(const AttnArgs& a, int skip_single, hipStream_t st) {
+  merge_kernel<ES, D><<<dim3((a.num_q_heads + 3) / 4, a.num_tokens), 256, 0, st>>>(a, skip_single);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma(const AttnArgs& a, bool has_chunks, void* header, hipStream_t st) {
+  hipError_t err;
+  if (has_chunks) {
+    // Query chunks on the persistent chunk kernel, single-token rows on the
+    // balanced decode; then the merge of split chunk rows.
+    if (a.max_query_len > 1) {
+      err = launch_prefill<D>(a, st);
+      if (err != hipSuccess) return err;
+    }
+    err = launch_streamk<D>(a, header, st);
+    if (err != hipSuccess) return err;
+    return a.max_splits > 1 ? launch_merge<2, D>(a, 1, st) : hipSuccess;
+  }
   const int G = a.num_q_heads / a.num_kv_heads;
   const unsigned z = (unsigned)a.num_seqs * a.num_kv_heads;
   const unsigned narrow_tiles = (unsigned)((G + 15) / 16);
-  if (has_chunks) {
-    constexpr int R = 2;
-    const unsigned tiles = (unsigned)(((int64_t)a.max_query_len * G + 16 * R - 1) / (16 * R));
-    attn_mfma_kernel<D, R><<<dim3(z, tiles, a.max_splits), 64, 0, st>>>(a, kMultiRowSeqs);
-    attn_mfma_kernel<D, 1><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a, kSingleRowSeqs);
-  } else {
-    attn_mfma_kernel<D, 1><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a, kAllSeqs);
-  }
-  return hipGetLastError();
+  attn_mfma_kernel<D, 1><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a, kAllSeqs);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return a.max_splits > 1 ? launch_merge<2, D>(a, 0, st) : hipSuccess;
 }
 
 template <int ES, int D>
 hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   const unsigned z = (unsigned)a.num_seqs * a.num_kv_heads;
   attn_valu_kernel<ES, D><<<dim3(z, a.max_query_len, a.max_splits), 64, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-template <int ES, int D>
-hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
-  merge_kernel<ES, D><<<dim3((a.num_q_heads + 3) / 4, a.max_query_len, a.num_seqs), 256, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
-  const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
-  // Resident waves: CU count times this kernel's occupancy at this LDS size
-  // (cached for the last device / sequence count seen).
-  static thread_local int c_dev = -1, c_seqs = -1, c_waves = 0;
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (dev != c_dev || a.num_seqs != c_seqs) {
-    int cus = 0, per_cu = 0;
-    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_streamk_kernel<D>, 64, lds);
-    if (err != hipSuccess) return err;
-    c_dev = dev;
-    c_seqs = a.num_seqs;
-    c_waves = cus * (per_cu > 0 ? per_cu : 1);
-  }
-  StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
-  decode_streamk_kernel<D><<<c_waves, 64, lds, st>>>(a, c_waves, hdr);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  merge_streamk_kernel<2, D><<<dim3((a.num_q_heads + 3) / 4, a.num_seqs), 256, 0, st>>>(a, hdr);
-  return hipGetLastError();
+  return a.max_splits > 1 ? launch_merge<ES, D>(a, 0, st) : hipSuccess;
 }
 
 }  // namespace
@@ -991,25 +1368,15 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, bool has_chunks, hipStream_t stream) {
-  hipError_t err;
-  const bool mfma = mfma_path(a);
-  if (mfma) {
-    err = a.head_dim == 128 ? launch_mfma<128>(a, has_chunks, stream)
-                            : launch_mfma<64>(a, has_chunks, stream);
-  } else if (a.bf16) {
-    err = a.head_dim == 128 ? launch_valu<2, 128>(a, stream) : launch_valu<2, 64>(a, stream);
-  } else {
-    err = a.head_dim == 128 ? launch_valu<4, 128>(a, stream) : launch_valu<4, 64>(a, stream);
+hipError_t launch_attention(const AttnArgs& a, bool has_chunks, void* header,
+                            hipStream_t stream) {
+  if (mfma_path(a)) {
+    return a.head_dim == 128 ? launch_mfma<128>(a, has_chunks, header, stream)
+                             : launch_mfma<64>(a, has_chunks, header, stream);
   }
-  if (err != hipSuccess) return err;
-  if (a.max_splits > 1) {
-    if (a.bf16)
-      err = a.head_dim == 128 ? launch_merge<2, 128>(a, stream) : launch_merge<2, 64>(a, stream);
-    else
-      err = a.head_dim == 128 ? launch_merge<4, 128>(a, stream) : launch_merge<4, 64>(a, stream);
-  }
-  return err;
+  if (a.bf16)
+    return a.head_dim == 128 ? launch_valu<2, 128>(a, stream) : launch_valu<2, 64>(a, stream);
+  return a.head_dim == 128 ? launch_valu<4, 128>(a, stream) : launch_valu<4, 64>(a, stream);
 }
 
 }  // namespace pa

@@ -46,7 +46,8 @@ def test_status_strings_and_version(lib):
 def test_workspace_queries(lib):
     n = lib.pa_decode_workspace_bytes(128, 64, 128, 8192, 16, 512)
     splits = 16
-    assert n == 128 * 64 * splits * 128 * 4 + 128 * 64 * splits * 2 * 4
+    # partials (o then (m, l), fp32) plus a header of 16 + 4 * (128 + 1) bytes rounded to 256
+    assert n == 128 * 64 * splits * 128 * 4 + 128 * 64 * splits * 2 * 4 + 768
     # balanced decode (split 0): up to ceil(256 steps / 8) + 1 = 33 pieces per row,
     # plus a header of 16 + 4 * (128 + 1) bytes rounded to 256
     assert lib.pa_decode_workspace_bytes(128, 64, 128, 8192, 16, 0) == \
@@ -56,7 +57,15 @@ def test_workspace_queries(lib):
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 100) == 0    # split not % 64
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 2048) > 0    # any multiple of 64
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 0, 16, 0) == 0
-    assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 0) > 0
+    # chunked prefill: chunk rows get ceil(8704 / 2048) = 5 split slots each; the
+    # balanced decode of single-token rows gets ceil(272 steps / 8) + 1 = 35 pieces
+    # per (sequence, head) row; header 16 + 4 * 65 bytes rounded to 256.
+    def al(x):
+        return -(-x // 256) * 256
+    assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 0) == \
+        al(2108 * 32 * 5 * 128 * 4) + al(2108 * 32 * 5 * 8) + al(64 * 32 * 35 * 128 * 4) + \
+        al(64 * 32 * 35 * 8) + 512
+    assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 96) == 0
 
 
 def _decode(lib, **kw):
@@ -73,6 +82,7 @@ def _decode(lib, **kw):
     (dict(lens=None), -1), (dict(dtype=7), -3), (dict(Hq=6, Hkv=4), -2),
     (dict(Hq=34, Hkv=2), -4), (dict(D=96), -4), (dict(B=12), -4), (dict(B=128), -4),
     (dict(maxb=0), -2), (dict(NB=0), -2), (dict(maxlen=0), -2), (dict(scale=float("nan")), -2),
+    (dict(scale=0.0), -2), (dict(scale=-0.1), -2),
     (dict(split=96), -2), (dict(ws=None), -5), (dict(wsb=16), -5), (dict(S=70000), -4),
 ])
 def test_decode_rejects_bad_arguments(lib, kw, code):
