@@ -20,6 +20,11 @@ What the oracle computes, and the passage each part follows:
   gather and textbook softmax attention in float64 ("03 -- PagedAttention &
   the vLLM V1 Architecture", section "The attention kernel side"; "Inside
   vLLM", section "Physical Block Mapping and Kernel Invocation").
+* ``fp8`` -- the e4m3 KV cache: per-(block, KV head) scales, quantisation
+  on the cache write (float32 division, clamp, round to nearest even) and
+  attention over the dequantised pools ("Tech Radar: vLLM v1 Production
+  Engine Architecture ...", section "Hopper TMA Warp Specialization & FP8
+  Kernel Integration", item "FP8 Block-Quantized Caching").
 * ``sizes`` -- the closed forms for block counts, KV bytes and internal
   fragmentation ("Tech Radar: vLLM v1 Production Engine Architecture ...",
   section "Mathematical Modeling of PagedAttention v3 Memory Bounds").
@@ -29,4 +34,4 @@ print, closed forms, special cases and brute force; none is "parity
 unpinned".
 """
 
-from . import block_manager, paged_attention, sizes  # noqa: F401
+from . import block_manager, fp8, paged_attention, sizes  # noqa: F401
