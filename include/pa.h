@@ -198,6 +198,62 @@ int pa_chunked_prefill(void* out, const void* query, const void* k_cache,
                        int32_t dtype, int32_t kv_split_tokens,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 (e4m3) KV cache.  The cache may hold K and V as 8-bit floats, one
+ * byte per element, quantised per block ("Tech Radar: vLLM v1 Production
+ * Engine Architecture ...", section "Hopper TMA Warp Specialization & FP8
+ * Kernel Integration", item "FP8 Block-Quantized Caching"; "High-Throughput
+ * Local LLM Infrastructure ...", FAQ "Q5").
+ *
+ * Format: OCP e4m3 (no infinities; 0x7F/0xFF are NaN; largest finite 448).
+ * Pools: uint8, K [num_blocks, num_kv_heads, block_size, head_dim] and
+ * V [num_blocks, num_kv_heads, head_dim, block_size], as the bf16 pools.
+ * Scales: k_scales and v_scales are float32 [num_blocks, num_kv_heads], one
+ * per (physical block, KV head), owned and set by the caller (for example
+ * when a block is allocated); the library only reads them.  The scales of
+ * every block a call touches must be finite and > 0 (checked under
+ * PA_CHECK=1, PA_ERR_INDEX otherwise).  Element x stored with scale s is
+ * code(x) = e4m3 of clamp(x / s, -448, 448) (float32 division, correctly
+ * rounded; round to nearest, ties to even); it stands for value(code) * s.
+ * block_size must be 16, 32 or 64 (PA_ERR_UNSUPPORTED otherwise).
+ * ---------------------------------------------------------------------- */
+
+/*
+ * pa_reshape_and_cache_fp8 -- as pa_reshape_and_cache, with bf16 key/value
+ * [num_tokens, num_kv_heads, head_dim] quantised into the e4m3 pools with
+ * the scales of each slot's (block, KV head).  Negative slots are skipped;
+ * two tokens aiming at one slot is undefined (PA_ERR_INDEX under PA_CHECK).
+ */
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                             void* v_cache, const float* k_scales,
+                             const float* v_scales,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks,
+                             void* stream);
+
+/* Workspace for pa_decode_fp8 (the balanced decode's pieces and header);
+ * 0 for invalid arguments. */
+size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t head_dim, int32_t max_seq_len,
+                                     int32_t block_size);
+
+/*
+ * pa_decode_fp8 -- pa_decode against e4m3 pools: bf16 query [num_seqs,
+ * num_q_heads, head_dim] and bf16 out; attention over the dequantised
+ * values value(code) * scale.  Always the balanced decode (no fixed split);
+ * at most 4096 sequences per call.  Other arguments as for pa_decode.
+ */
+int pa_decode_fp8(void* out, const void* query, const void* k_cache,
+                  const void* v_cache, const float* k_scales,
+                  const float* v_scales, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                  const int32_t* seq_lens, int32_t num_seqs,
+                  int32_t max_seq_len, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

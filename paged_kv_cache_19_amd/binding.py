@@ -39,6 +39,11 @@ SIGNATURES = {
     "pa_chunked_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _i32, _vp, _sz, _vp]),
+    "pa_reshape_and_cache_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                _i32, _i32, _i32, _vp]),
+    "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
 }
 
 
@@ -154,9 +159,8 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     NB, Hkv, B, _ = k_cache.shape
     if out is None:
         out = torch.empty_like(query)
-    if workspace is None:
-        # zero-filled: the balanced decode keeps piece counters in it
-        workspace = torch.zeros(decode_workspace_bytes(S, Hq, D, max_seq_len, B, kv_split_tokens),
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(decode_workspace_bytes(S, Hq, D, max_seq_len, B, kv_split_tokens),
                                 dtype=torch.uint8, device=query.device)
     _check("pa_decode", lib().pa_decode(
         _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
@@ -178,8 +182,8 @@ def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     S = seq_lens.numel()
     if out is None:
         out = torch.empty_like(query)
-    if workspace is None:
-        workspace = torch.zeros(chunked_prefill_workspace_bytes(S, T, Hq, D, max_seq_len, B,
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(chunked_prefill_workspace_bytes(S, T, Hq, D, max_seq_len, B,
                                                                 kv_split_tokens),
                                 dtype=torch.uint8, device=query.device)
     _check("pa_chunked_prefill", lib().pa_chunked_prefill(
@@ -188,4 +192,67 @@ def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
         T, max_seq_len,
         max_query_len, Hq, Hkv, D, B, NB, scale, _dtype(query), kv_split_tokens,
         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+# -- FP8 (e4m3) KV cache -------------------------------------------------------
+
+def _fp8_pool(t: torch.Tensor) -> None:
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError(f"an fp8 pool is uint8 or float8_e4m3fn, not {t.dtype}")
+
+
+def _f32(t: torch.Tensor) -> None:
+    if t.dtype != torch.float32:
+        raise ValueError("scales are float32 [num_blocks, num_kv_heads]")
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
+                          slot_mapping: torch.Tensor, stream=None) -> None:
+    T, H, D = key.shape
+    NB, _, B, _ = k_cache.shape
+    if key.dtype != torch.bfloat16 or value.dtype != torch.bfloat16:
+        raise ValueError("key/value are bf16")
+    _fp8_pool(k_cache)
+    _fp8_pool(v_cache)
+    _f32(k_scales)
+    _f32(v_scales)
+    _check("pa_reshape_and_cache_fp8", lib().pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(slot_mapping), T, H, D, B, NB, _stream(stream)))
+
+
+def decode_fp8_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, block_size) -> int:
+    n = lib().pa_decode_fp8_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                            block_size)
+    if n == 0:
+        raise PAError("pa_decode_fp8_workspace_bytes", -2)
+    return n
+
+
+def decode_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               k_scales: torch.Tensor, v_scales: torch.Tensor, block_tables: torch.Tensor,
+               seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+               block_refcounts: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = k_cache.shape
+    if query.dtype != torch.bfloat16:
+        raise ValueError("the fp8 decode takes a bf16 query")
+    _fp8_pool(k_cache)
+    _fp8_pool(v_cache)
+    _f32(k_scales)
+    _f32(v_scales)
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(decode_fp8_workspace_bytes(S, Hq, D, max_seq_len, B),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_decode_fp8", lib().pa_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
+        max_seq_len, Hq, Hkv, D, B, NB, scale, _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return out

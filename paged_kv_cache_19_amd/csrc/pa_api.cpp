@@ -146,13 +146,58 @@ int validate_slots(const int64_t* d_slots, int num_tokens, int64_t num_slots, hi
   return PA_OK;
 }
 
+// PA_CHECK for the fp8 cache: the K and V scales of every listed block must
+// be finite and > 0.
+int validate_scales(const float* d_ks, const float* d_vs, int num_blocks, int num_kv_heads,
+                    const std::vector<int64_t>& blocks, hipStream_t st) {
+  if (blocks.empty()) return PA_OK;
+  if (!d_ks || !d_vs) return PA_ERR_NULL;
+  const size_t n = (size_t)num_blocks * num_kv_heads;
+  std::vector<float> ks(n), vs(n);
+  if (hipMemcpyAsync(ks.data(), d_ks, n * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(vs.data(), d_vs, n * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  for (int64_t b : blocks) {
+    for (int h = 0; h < num_kv_heads; ++h) {
+      const float k = ks[(size_t)b * num_kv_heads + h], v = vs[(size_t)b * num_kv_heads + h];
+      if (!isfinite(k) || !(k > 0.f) || !isfinite(v) || !(v > 0.f)) return PA_ERR_INDEX;
+    }
+  }
+  return PA_OK;
+}
+
+// Blocks the tables of a (validated) batch hold.
+int table_blocks_used(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, int num_seqs,
+                      int block_size, hipStream_t st, std::vector<int64_t>* out) {
+  std::vector<int32_t> bt((size_t)num_seqs * max_blocks), lens(num_seqs);
+  if (hipMemcpyAsync(bt.data(), d_bt, bt.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(lens.data(), d_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int nb = (lens[s] + block_size - 1) / block_size;
+    for (int b = 0; b < nb; ++b) out->push_back(bt[(size_t)s * max_blocks + b]);
+  }
+  return PA_OK;
+}
+
+// fp8 cache arguments of the attention entry points (kv_fp8 = 0: none).
+struct Fp8Kv {
+  int kv_fp8 = 0;
+  const float* k_scales = nullptr;
+  const float* v_scales = nullptr;
+};
+
 int attention_common(void* out, const void* query, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int max_blocks, const int32_t* refcounts,
                      const int32_t* seq_lens,
                      const int32_t* qsl, int num_seqs, int num_tokens, int max_seq_len,
                      int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int block_size, int num_blocks, float scale, int dtype, int kv_split_tokens,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream,
+                     const Fp8Kv& f8 = Fp8Kv()) {
   int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
   if (num_seqs < 0 || num_tokens < 0 || max_blocks <= 0 || num_blocks <= 0 ||
@@ -160,6 +205,7 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
+  if (f8.kv_fp8 && (!f8.k_scales || !f8.v_scales)) return PA_ERR_NULL;
   if ((int64_t)num_seqs * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   WorkspacePlan plan;
   const bool chunk_entry = qsl != nullptr;
@@ -184,6 +230,13 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     rc = validate_metadata(block_tables, max_blocks, seq_lens, qsl, num_seqs, num_tokens,
                            max_seq_len, max_query_len, block_size, num_blocks, st);
     if (rc != PA_OK) return rc;
+    if (f8.kv_fp8) {
+      std::vector<int64_t> used;
+      rc = table_blocks_used(block_tables, max_blocks, seq_lens, num_seqs, block_size, st, &used);
+      if (rc == PA_OK)
+        rc = validate_scales(f8.k_scales, f8.v_scales, num_blocks, num_kv_heads, used, st);
+      if (rc != PA_OK) return rc;
+    }
   }
   char* ws = static_cast<char*>(workspace);
   a.q = query;
@@ -207,6 +260,9 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   a.max_splits = plan.max_splits;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.kv_fp8 = f8.kv_fp8;
+  a.k_scales = f8.k_scales;
+  a.v_scales = f8.v_scales;
   void* header = ws + plan.a_o + plan.a_ml + plan.b_o + plan.b_ml;
   hipError_t err;
   if (chunk_entry) {
@@ -220,6 +276,7 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     a.sk_slots = plan.max_pieces;
     err = pa::launch_decode_streamk(a, header, st);
   } else {
+    if (a.kv_fp8) return PA_ERR_UNSUPPORTED;  // the fp8 cache has the balanced decode only
     err = pa::launch_attention(a, false, nullptr, st);
   }
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -342,6 +399,67 @@ int pa_chunked_prefill(void* out, const void* query, const void* k_cache, const 
                           max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
                           num_blocks, scale, dtype, kv_split_tokens, workspace,
                           workspace_bytes, stream);
+}
+
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const float* k_scales, const float* v_scales,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 64) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
+    return PA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    int rc = validate_slots(slot_mapping, num_tokens, num_slots, st);
+    if (rc != PA_OK) return rc;
+    std::vector<int64_t> slots(num_tokens), blocks;
+    if (hipMemcpyAsync(slots.data(), slot_mapping, slots.size() * 8, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return PA_ERR_HIP;
+    for (int64_t s : slots)
+      if (s >= 0) blocks.push_back(s / block_size);
+    rc = validate_scales(k_scales, v_scales, num_blocks, num_kv_heads, blocks, st);
+    if (rc != PA_OK) return rc;
+  }
+  return pa::launch_reshape_and_cache_fp8(key, value, k_cache, v_cache, k_scales, v_scales,
+                                          slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                          block_size, num_blocks, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t max_seq_len, int32_t block_size) {
+  if (block_size < 16) return 0;
+  return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, block_size, 0);
+}
+
+int pa_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                  const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                  int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                  const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t num_blocks, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  // The fp8 decode runs on the balanced kernel only (block_size >= 16: a
+  // lane's 16 consecutive keys share one block and so one scale).
+  if (block_size > 0 && block_size < 16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  Fp8Kv f8;
+  f8.kv_fp8 = 1;
+  f8.k_scales = k_scales;
+  f8.v_scales = v_scales;
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                          PA_BF16, 0, workspace, workspace_bytes, stream, f8);
 }
 
 }  // extern "C"

@@ -28,7 +28,10 @@ struct AttnArgs {
   int32_t split_tokens, max_splits, max_query_len;
   int32_t sk_slots;         // pieces per row in sk_part_*
   float scale_log2;         // scale * log2(e)
-  int32_t bf16;             // 1: bf16 elements, 0: fp32
+  int32_t bf16;             // 1: bf16 elements, 0: fp32 (q, out and, unless kv_fp8, the cache)
+  int32_t kv_fp8;           // 1: e4m3 cache with per-(block, KV head) scales, bf16 q/out
+  const float* k_scales;    // [NB, Hkv] (kv_fp8 only)
+  const float* v_scales;    // [NB, Hkv]
 };
 
 // Balanced decode: every resident wave streams at least this many 32-key
@@ -51,6 +54,15 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int32_t num_blocks, int32_t elem_bytes,
                                     hipStream_t stream);
 
+// Cache write into e4m3 pools (bf16 K/V in), quantised with the scale of
+// each slot's (block, KV head).
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                        void* v_cache, const float* k_scales,
+                                        const float* v_scales, const int64_t* slots,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        hipStream_t stream);
+
 // Split-K attention pass (writes final rows for single-split rows and
 // partials otherwise), then the log-sum-exp merge pass when needed.
 // ``has_chunks``: rows of multi-token sequences go to the persistent chunk
@@ -64,7 +76,7 @@ hipError_t launch_attention(const AttnArgs& a, bool has_chunks, void* header,
 constexpr int kMaxChunkSeqs = 2048;
 
 // Balanced ("stream-K") decode over a fixed set of resident waves, then the
-// merge of the pieces.  ``header`` is workspace for the step prefix sums
+// merge of the pieces (bf16 or, with a.kv_fp8, e4m3 cache).  ``header`` is workspace for the step prefix sums
 // (16 + 4 * (num_seqs + 1) bytes); a.max_splits is the piece capacity per row.
 hipError_t launch_decode_streamk(const AttnArgs& a, void* header, hipStream_t stream);
 

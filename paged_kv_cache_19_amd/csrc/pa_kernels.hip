@@ -172,6 +172,75 @@ __global__ __launch_bounds__(16 * D * ES / 16) void reshape_and_cache_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// reshape_and_cache into an fp8 (e4m3) cache.  Each element x of a bf16 K/V
+// row becomes the e4m3 code of clamp(x / s, -448, 448), rounded to nearest
+// even, with s the scale of the (block, KV head) the slot lies in; the
+// division is the correctly rounded float32 one.  One thread converts 8
+// elements of one token: 16 tokens of one KV head per workgroup.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t quant4_e4m3(float a, float b, float c, float d) {
+  uint32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+}
+
+__device__ __forceinline__ float sat_e4m3(float y) { return fminf(fmaxf(y, -448.f), 448.f); }
+
+template <int D>
+__global__ __launch_bounds__(2 * D) void reshape_and_cache_fp8_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales,
+    const int64_t* __restrict__ slots, int ntok, int H, int lg, int64_t num_slots) {
+  constexpr int NG = D / 8;  // 8-element groups per head row
+  const int B = 1 << lg;
+  const int h = blockIdx.y;
+  const int t = blockIdx.x * 16 + threadIdx.x / NG;
+  const int g = threadIdx.x % NG;
+  if (t >= ntok) return;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot >> lg;
+  const int off = (int)(slot & (B - 1));
+  const int64_t src = ((int64_t)t * H + h) * D + 8 * g;
+  {
+    const float ks = k_scales[blk * H + h];
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(key + src);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(raw[e] << 16);
+      x[2 * e + 1] = __uint_as_float(raw[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sat_e4m3(__fdiv_rn(x[e], ks));
+    uint2 q;
+    q.x = quant4_e4m3(x[0], x[1], x[2], x[3]);
+    q.y = quant4_e4m3(x[4], x[5], x[6], x[7]);
+    *reinterpret_cast<uint2*>(k_cache + ((blk * H + h) * B + off) * D + 8 * g) = q;
+  }
+  {
+    const float vs = v_scales[blk * H + h];
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(value + src);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(raw[e] << 16);
+      x[2 * e + 1] = __uint_as_float(raw[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sat_e4m3(__fdiv_rn(x[e], vs));
+    const uint32_t lo = quant4_e4m3(x[0], x[1], x[2], x[3]);
+    const uint32_t hi = quant4_e4m3(x[4], x[5], x[6], x[7]);
+    uint8_t* dst = v_cache + ((blk * H + h) * D + 8 * g) * B + off;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[(int64_t)e * B] = (lo >> (8 * e)) & 0xFF;
+      dst[(int64_t)(e + 4) * B] = (hi >> (8 * e)) & 0xFF;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 attention on MFMA.
 //
 // One wave serves one (sequence, KV head, row-tile group, context split).
@@ -247,7 +316,11 @@ __device__ __forceinline__ SeqView seq_view(const AttnArgs& a, int s, int kvh, i
 // Load the query rows row0 .. row0 + 16R - 1 of a sequence (row = j * G + g
 // for chunk token j and group head g) into B-operand fragments, and reset
 // the softmax state.  Rows past the sequence are zero and see no keys.
-template <int D, int R>
+//
+// With FP8DIMS the head_dim order inside the operands is the one of the fp8
+// path: slice kk, lane group j4, element e holds dim (D/4)*j4 + 8*kk + e
+// (any order gives the same dot product as long as K uses it too).
+template <int D, int R, bool FP8DIMS = false>
 __device__ __forceinline__ void load_rows(const AttnArgs& a, const SeqView& v, int row0,
                                           RowState<D, R>& st) {
   constexpr int KK = D / 32;
@@ -265,10 +338,10 @@ __device__ __forceinline__ void load_rows(const AttnArgs& a, const SeqView& v, i
       const int j = row / G;
       const int g = row - j * G;
       st.klim[t] = min(v.L - v.qn + j + 1, v.kcap);
-      const uint16_t* qp =
-          q + ((int64_t)(v.r0 + j) * a.num_q_heads + v.kvh * G + g) * D + 8 * j4;
+      const uint16_t* qp = q + ((int64_t)(v.r0 + j) * a.num_q_heads + v.kvh * G + g) * D +
+                           (FP8DIMS ? (D / 4) * j4 : 8 * j4);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) st.qf[t][kk] = load_bf16x8(qp + 32 * kk);
+      for (int kk = 0; kk < KK; ++kk) st.qf[t][kk] = load_bf16x8(qp + (FP8DIMS ? 8 : 32) * kk);
     } else {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) st.qf[t][kk] = bf16x8{};
@@ -449,6 +522,191 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode over an fp8 (e4m3) cache: 64 keys per step.
+//
+// Every e4m3 value is exactly a bf16 value, so K and V codes are widened to
+// bf16 in registers and the bf16 MFMA does the products; the per-(block,
+// KV head) scales are applied to the scores (K) and to the probabilities
+// before the PV product (V), never to the 448-range codes themselves.
+//
+// QK^T: four MFMAs per head_dim slice ("a".."d", x = 0..3); MFMA x row i is
+// token 16*(i/4) + 4x + i%4 of the step, so lane l ends up holding the
+// scores of tokens 16*(l/16) + 0..15 (register 4x + r = token 4x + r of the
+// lane's group of 16) for query row l%16.  A lane's K operand is one token
+// row's D/4 consecutive bytes, dims (D/4)*(l/16) + 8*kk + e for slice kk
+// (the query uses the same order).  PV: the lane's 16 probabilities are the
+// A operand of two MFMAs (tokens 16*(l/16) + 0..7 and + 8..15); the B
+// operand is one 16-byte load of 16 consecutive tokens of one head_dim
+// column from the [D, B] V layout (B >= 16, so the group of 16 tokens sits
+// in one block and so has one K and one V scale).
+// ---------------------------------------------------------------------------
+template <int D>
+struct KVFrag8 {
+  u32x4 k[4][D / 64];  // x = 0..3: the lane's D/4 bytes of one token row
+  u32x4 v[D / 16];     // 16 tokens of head_dim column 16*n + l%16
+  float ks, vs;        // scales of the block of the lane's 16 tokens
+};
+
+// Eight e4m3 codes (two dwords, lowest byte first) as bf16, exactly.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(a[0]);
+  r[1] = static_cast<__bf16>(a[1]);
+  r[2] = static_cast<__bf16>(b[0]);
+  r[3] = static_cast<__bf16>(b[1]);
+  r[4] = static_cast<__bf16>(c[0]);
+  r[5] = static_cast<__bf16>(c[1]);
+  r[6] = static_cast<__bf16>(d[0]);
+  r[7] = static_cast<__bf16>(d[1]);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p, bool stream) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return stream ? __builtin_nontemporal_load(q) : *q;
+}
+
+template <int D, bool STREAM>
+__device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, int kv_wave,
+                                           int kv_min, int k_begin, int k_end,
+                                           RowState<D, 1>& st) {
+  constexpr int KK = D / 32;
+  constexpr int KP = D / 64;
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15;
+  const int j4 = lane >> 4;
+  const int lg = a.log2_block;
+  const int B = 1 << lg;
+  const int Hkv = a.num_kv_heads;
+  const int64_t trow = (int64_t)v.s * a.max_blocks;
+  auto window = [&](int b0) {
+    const int x = a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)];
+    return clampi(x, 0, a.num_blocks - 1);
+  };
+  int blk0 = k_begin >> lg;
+  int wid = window(blk0);
+  int wid_next = window(blk0 + 64);
+  auto block_id = [&](int pos) { return __shfl(wid, min(pos >> lg, v.nblk - 1) - blk0); };
+
+  const int64_t blk_stride = (int64_t)Hkv * B * D;  // bytes
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + (int64_t)v.kvh * B * D + (D / 4) * j4;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + (int64_t)v.kvh * D * B + (int64_t)i * B;
+  const int tok_k = 16 * (i >> 2) + (i & 3);
+  const float sl2 = a.scale_log2;
+
+  auto load = [&](KVFrag8<D>& f, int c) {
+    if ((c >> lg) - blk0 >= 64) {  // wave-uniform: enter the next window
+      blk0 += 64;
+      wid = wid_next;
+      wid_next = window(blk0 + 64);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int pos = c + tok_k + 4 * x;
+      const uint8_t* kp = kbase + block_id(pos) * blk_stride + (int64_t)(pos & (B - 1)) * D;
+#pragma unroll
+      for (int p = 0; p < KP; ++p) f.k[x][p] = load_u32x4(kp + 16 * p, STREAM);
+    }
+    const int pv = c + 16 * j4;
+    const int bv = block_id(pv);
+    const uint8_t* vp = vbase + bv * blk_stride + (pv & (B - 1));
+#pragma unroll
+    for (int n = 0; n < NT; ++n) f.v[n] = load_u32x4(vp + (int64_t)16 * n * B, STREAM);
+    f.ks = a.k_scales[(int64_t)bv * Hkv + v.kvh];
+    f.vs = a.v_scales[(int64_t)bv * Hkv + v.kvh];
+  };
+
+  auto compute = [&](KVFrag8<D>& f, int c) {
+    const int pv = c + 16 * j4;
+    f32x4 s4[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) s4[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const u32x4 w = f.k[x][kk >> 1];
+        const bf16x8 kf = e4m3x8_to_bf16(w[2 * (kk & 1)], w[2 * (kk & 1) + 1]);
+        s4[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, st.qf[0][kk], s4[x], 0, 0, 0);
+      }
+    }
+    const float kscale = f.ks * sl2;
+    float sv[16];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[4 * x + r] = s4[x][r] * kscale;
+    if (c + 64 > kv_min) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[e] = (pv + e < st.klim[0]) ? sv[e] : neg_inf();
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+    mx = xl_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > st.m[0] + kLazyRescaleLog2) != 0) {
+      const float mnew = fmaxf(st.m[0], mx);
+      const float alpha = fast_exp2(st.m[0] - ((mnew == neg_inf()) ? 0.f : mnew));
+      st.l[0] *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * j4 + r);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.o[0][n][r] *= ar[r];
+      st.m[0] = mnew;
+    }
+    const float muse = (st.m[0] == neg_inf()) ? 0.f : st.m[0];
+    float ps = 0.f;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = fast_exp2(sv[e] - muse);
+      ps += p;
+      pf[e >> 3][e & 7] = static_cast<__bf16>(p * f.vs);
+    }
+    st.l[0] += xl_sum(ps);
+    const bool tail = c + 64 > kv_wave;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 vf = e4m3x8_to_bf16(f.v[n][2 * h2], f.v[n][2 * h2 + 1]);
+        if (tail) {
+          // keys past the last visible one may be unwritten slots (NaN codes)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (pv + 8 * h2 + e >= kv_wave) vf[e] = static_cast<__bf16>(0.f);
+        }
+        st.o[0][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[h2], vf, st.o[0][n], 0, 0, 0);
+      }
+    }
+  };
+
+  // Two fragment sets, loaded one step ahead (the last prefetch re-reads the
+  // final step so that every iteration issues the same loads).
+  KVFrag8<D> f0, f1;
+  int c = k_begin;
+  load(f0, c);
+  while (true) {
+    load(f1, c + 64 < k_end ? c + 64 : c);
+    compute(f0, c);
+    c += 64;
+    if (c >= k_end) break;
+    load(f0, c + 64 < k_end ? c + 64 : c);
+    compute(f1, c);
+    c += 64;
+    if (c >= k_end) break;
+  }
+}
+
 // Where a wave's partial (o, m, l) rows go: ``slots`` partials per row,
 // row index = row_base + head when row_base >= 0, else the output row.
 struct PartialDst {
@@ -591,9 +849,13 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t g, int64_t waves, int64_
   return ((g + 1) * waves - 1) / total;
 }
 
-template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_streamk_kernel(AttnArgs a, int waves,
-                                                            StreamKHeader* hdr) {
+// FP8: the cache is e4m3 with per-(block, KV head) scales and a step is 64
+// keys (the bf16 cache steps 32 keys at a time).
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_streamk_kernel(
+    AttnArgs a, int waves, StreamKHeader* hdr) {
+  constexpr int STEP = FP8 ? 64 : 32;
+  constexpr int LSTEP = FP8 ? 6 : 5;
   extern __shared__ int smem[];
   const int S = a.num_seqs;
   int* P = smem;           // [S + 1] steps before sequence s (per KV head)
@@ -608,7 +870,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
     const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
     // Only single-token rows are decode work (query chunks have their own kernel).
-    P[s + 1] = (qn == 1 && kl > 0) ? (kl + 31) >> 5 : 0;
+    P[s + 1] = (qn == 1 && kl > 0) ? (kl + STEP - 1) >> LSTEP : 0;
     Ls[s] = L;
   }
   __syncthreads();
@@ -672,12 +934,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const SeqView v = seq_view(a, s, kvh, Ls[s], r0, 1);
     const int kl = min(v.L, v.kcap);
     RowState<D, 1> st;
-    load_rows<D, 1>(a, v, 0, st);
-    const int k_begin = c0 * 32;
-    const int k_end = min(c1 * 32, kl);
-    const int k_sh = k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) : 0;
-    if (k_sh > k_begin) attend<D, 1, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
-    if (k_end > max(k_begin, k_sh)) attend<D, 1, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+    load_rows<D, 1, FP8>(a, v, 0, st);
+    const int k_begin = c0 * STEP;
+    const int k_end = min(c1 * STEP, kl);
+    const int k_sh =
+        k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) & ~(STEP - 1) : 0;
+    if constexpr (FP8) {
+      if (k_sh > k_begin) attend_fp8<D, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+      if (k_end > max(k_begin, k_sh))
+        attend_fp8<D, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+    } else {
+      if (k_sh > k_begin) attend<D, 1, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+      if (k_end > max(k_begin, k_sh))
+        attend<D, 1, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+    }
     write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
                      PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
     g += c1 - c0;
@@ -1265,15 +1535,15 @@ hipError_t resident(Residency& c, K kernel, int threads, size_t lds, int seqs, i
   return hipSuccess;
 }
 
-template <int D>
+template <int D, bool FP8 = false>
 hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
   static thread_local Residency cache;
   const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
   int waves = 0;
-  hipError_t err = resident(cache, decode_streamk_kernel<D>, 64, lds, a.num_seqs, waves);
+  hipError_t err = resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, a.num_seqs, waves);
   if (err != hipSuccess) return err;
   StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
-  decode_streamk_kernel<D><<<waves, 64, lds, st>>>(a, waves, hdr);
+  decode_streamk_kernel<D, FP8><<<waves, 64, lds, st>>>(a, waves, hdr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   merge_streamk_kernel<2, D><<<dim3((a.num_q_heads + 3) / 4, a.num_seqs), 256, 0, st>>>(a, hdr);
@@ -1333,6 +1603,9 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode_streamk(const AttnArgs& a, void* header, hipStream_t stream) {
+  if (a.kv_fp8)
+    return a.head_dim == 128 ? launch_streamk<128, true>(a, header, stream)
+                             : launch_streamk<64, true>(a, header, stream);
   return a.head_dim == 128 ? launch_streamk<128>(a, header, stream)
                            : launch_streamk<64>(a, header, stream);
 }
@@ -1365,6 +1638,28 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   else if (elem_bytes == 4 && head_dim == 128) PA_RC(4, 128);
   else PA_RC(4, 64);
 #undef PA_RC
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                        void* v_cache, const float* k_scales,
+                                        const float* v_scales, const int64_t* slots,
+                                        int32_t num_tokens, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        hipStream_t stream) {
+  const int lg = __builtin_ctz((unsigned)block_size);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const dim3 grid((num_tokens + 15) / 16, num_kv_heads);
+  const uint16_t* k = static_cast<const uint16_t*>(key);
+  const uint16_t* v = static_cast<const uint16_t*>(value);
+  uint8_t* kc = static_cast<uint8_t*>(k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(v_cache);
+  if (head_dim == 128)
+    reshape_and_cache_fp8_kernel<128><<<grid, 256, 0, stream>>>(
+        k, v, kc, vc, k_scales, v_scales, slots, num_tokens, num_kv_heads, lg, num_slots);
+  else
+    reshape_and_cache_fp8_kernel<64><<<grid, 128, 0, stream>>>(
+        k, v, kc, vc, k_scales, v_scales, slots, num_tokens, num_kv_heads, lg, num_slots);
   return hipGetLastError();
 }
 

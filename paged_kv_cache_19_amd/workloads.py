@@ -29,6 +29,14 @@ Workload shapes (one attention layer; "G" = query heads per KV head):
    chunk after U[1024, 8192] cached tokens, then 60 decode sequences of
    U[256, 4096] tokens; 32/8 heads, head dim 128, block size 16.
 
+With ``kv_fp8`` the workload also carries an e4m3 KV cache: uint8 pools
+``k_cache8`` / ``v_cache8`` (same layouts as the bf16 pools) of uniformly
+drawn codes, the two NaN codes left out, and float32 scales ``k_scales`` /
+``v_scales`` of shape ``[NB, H_kv]`` drawn uniformly from [2/448, 4/448]
+(what an amax of 2 to 4 would give), so the dequantised values stay within
++-4 like the N(0, 1) values of the bf16 pools.  They come from a generator of their
+own, so the bf16 tensors are the same with or without them.
+
 Lengths are inclusive uniform integers.  ``seq_lens`` counts every token
 including this step's new ones; the query rows of sequence s are its last
 ``q_len`` positions.
@@ -163,7 +171,7 @@ def make_workload(cfg: int, seed: Optional[int] = None, device: str = "cpu",
                   q_lens: Optional[List[int]] = None,
                   shape: Optional[Shape] = None,
                   shared_prefix_tokens: Optional[int] = None,
-                  num_blocks: Optional[int] = None) -> Workload:
+                  num_blocks: Optional[int] = None, kv_fp8: bool = False) -> Workload:
     """Draw workload ``cfg`` (1..5) with ``seed`` (default 1000 + cfg).
 
     ``seq_lens``/``q_lens``/``shape``/``shared_prefix_tokens``/``num_blocks``
@@ -212,6 +220,8 @@ def make_workload(cfg: int, seed: Optional[int] = None, device: str = "cpu",
                   max(blocks_per_seq) + 1, device)
     if materialize:
         _draw_values(wl)
+        if kv_fp8:
+            _draw_fp8_cache(wl)
     return wl
 
 
@@ -233,3 +243,24 @@ def _draw_values(wl: Workload) -> None:
     wl.tensors["key"] = randn(T, H, D)
     wl.tensors["value"] = randn(T, H, D)
     wl.tensors["query"] = randn(T, Hq, D)
+
+
+def _draw_fp8_cache(wl: Workload) -> None:
+    """Uniform e4m3 codes (NaN codes 0x7F/0xFF excluded) and uniform scales."""
+    shp = wl.shape
+    gen = torch.Generator(device=wl.device)
+    gen.manual_seed(wl.seed + 7919)
+    NB, H, B, D = wl.num_blocks, shp.num_kv_heads, shp.block_size, shp.head_dim
+
+    def codes(*size):
+        c = torch.randint(0, 254, size, generator=gen, device=wl.device, dtype=torch.int32)
+        return (c + (c >= 127).to(torch.int32)).to(torch.uint8)   # skip 0x7F; 0xFF unreachable
+
+    def scales():
+        return torch.rand(NB, H, generator=gen, device=wl.device,
+                          dtype=torch.float32) * (2.0 / 448) + 2.0 / 448
+
+    wl.tensors["k_cache8"] = codes(NB, H, B, D)
+    wl.tensors["v_cache8"] = codes(NB, H, D, B)
+    wl.tensors["k_scales"] = scales()
+    wl.tensors["v_scales"] = scales()
