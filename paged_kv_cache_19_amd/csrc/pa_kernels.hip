@@ -287,6 +287,11 @@ struct KVFrag {
 // are then at most 2^8 and the final o / l is unchanged.
 constexpr float kLazyRescaleLog2 = 8.f;
 
+// Keeps the (rarely taken) rescale branch a branch: without it the compiler
+// turns the block into selects and multiplies the whole accumulator on
+// every step.
+__device__ __forceinline__ void rare_branch() { __asm__ volatile(""); }
+
 // Query rows of one wave (R tiles of 16) and their online-softmax state.
 template <int D, int R>
 struct RowState {
@@ -476,6 +481,7 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
       mx = xl_max(mx);
       if (__builtin_amdgcn_ballot_w64(mx > st.m[t] + kLazyRescaleLog2) != 0) {
+        rare_branch();
         const float mnew = fmaxf(st.m[t], mx);
         const float alpha = fast_exp2(st.m[t] - ((mnew == neg_inf()) ? 0.f : mnew));
         st.l[t] *= alpha;
@@ -622,8 +628,23 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
     f.vs = a.v_scales[(int64_t)bv * Hkv + v.kvh];
   };
 
-  auto compute = [&](KVFrag8<D>& f, int c) {
+  // MASK: the step holds keys at or past kv_min (scores masked to -inf)
+  // or kv_wave (V codes zeroed: they may be unwritten NaN slots).  Only the
+  // last step of a piece can; the others run without any per-key test.
+  auto compute = [&](KVFrag8<D>& f, int c, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int pv = c + 16 * j4;
+    if constexpr (MASK) {
+      // zero the V bytes of keys >= kv_wave (16 keys per lane, 4 per dword)
+      const int nv = clampi(kv_wave - pv, 0, 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int n_in = clampi(nv - 4 * w, 0, 4);
+        const uint32_t keep = n_in >= 4 ? 0xFFFFFFFFu : ((1u << (8 * n_in)) - 1u);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) f.v[n][w] &= keep;
+      }
+    }
     f32x4 s4[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) s4[x] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -642,15 +663,17 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[4 * x + r] = s4[x][r] * kscale;
-    if (c + 64 > kv_min) {
+    if constexpr (MASK) {
+      const int lim = st.klim[0] - pv;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sv[e] = (pv + e < st.klim[0]) ? sv[e] : neg_inf();
+      for (int e = 0; e < 16; ++e) sv[e] = (e < lim) ? sv[e] : neg_inf();
     }
     float mx = sv[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
     mx = xl_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > st.m[0] + kLazyRescaleLog2) != 0) {
+      rare_branch();
       const float mnew = fmaxf(st.m[0], mx);
       const float alpha = fast_exp2(st.m[0] - ((mnew == neg_inf()) ? 0.f : mnew));
       st.l[0] *= alpha;
@@ -673,37 +696,41 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
       pf[e >> 3][e & 7] = static_cast<__bf16>(p * f.vs);
     }
     st.l[0] += xl_sum(ps);
-    const bool tail = c + 64 > kv_wave;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 vf = e4m3x8_to_bf16(f.v[n][2 * h2], f.v[n][2 * h2 + 1]);
-        if (tail) {
-          // keys past the last visible one may be unwritten slots (NaN codes)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (pv + 8 * h2 + e >= kv_wave) vf[e] = static_cast<__bf16>(0.f);
-        }
+        const bf16x8 vf = e4m3x8_to_bf16(f.v[n][2 * h2], f.v[n][2 * h2 + 1]);
         st.o[0][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[h2], vf, st.o[0][n], 0, 0, 0);
       }
     }
   };
 
+  // Steps below k_safe need no mask; at most one step (the last) does.
   // Two fragment sets, loaded one step ahead (the last prefetch re-reads the
   // final step so that every iteration issues the same loads).
+  const int k_safe = max(k_begin, min(k_end, (min(kv_min, kv_wave) - k_begin) / 64 * 64 + k_begin));
   KVFrag8<D> f0, f1;
   int c = k_begin;
-  load(f0, c);
-  while (true) {
-    load(f1, c + 64 < k_end ? c + 64 : c);
-    compute(f0, c);
-    c += 64;
-    if (c >= k_end) break;
-    load(f0, c + 64 < k_end ? c + 64 : c);
-    compute(f1, c);
-    c += 64;
-    if (c >= k_end) break;
+  if (c < k_safe) {
+    load(f0, c);
+    while (true) {
+      load(f1, c + 64 < k_end ? c + 64 : c);
+      compute(f0, c, std::false_type());
+      c += 64;
+      if (c >= k_safe) break;
+      load(f0, c + 64 < k_end ? c + 64 : c);
+      compute(f1, c, std::false_type());
+      c += 64;
+      if (c >= k_safe) {
+        f1 = f0;
+        break;
+      }
+    }
+    if (c < k_end) compute(f1, c, std::true_type());  // prefetched by the last iteration
+  } else if (c < k_end) {
+    load(f1, c);
+    compute(f1, c, std::true_type());
   }
 }
 
@@ -1232,6 +1259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         mx = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])) * sl2;
       }
       if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescaleLog2) != 0) {
+        rare_branch();
         const float mnew = fmaxf(m, mx);
         const float alpha = fast_exp2(m - ((mnew == neg_inf()) ? 0.f : mnew));
         l *= alpha;
