@@ -20,6 +20,10 @@ What the oracle computes, and the passage each part follows:
   gather and textbook softmax attention in float64 ("03 -- PagedAttention &
   the vLLM V1 Architecture", section "The attention kernel side"; "Inside
   vLLM", section "Physical Block Mapping and Kernel Invocation").
+* ``block_ops`` -- whole-block copies between pools: copy-on-write inside
+  a pool and swapping to and from a host pool ("03 -- PagedAttention & the
+  vLLM V1 Architecture", sections "The block table walkthrough" and
+  "Preemption & eviction").
 * ``fp8`` -- the e4m3 KV cache: per-(block, KV head) scales, quantisation
   on the cache write (float32 division, clamp, round to nearest even) and
   attention over the dequantised pools ("Tech Radar: vLLM v1 Production
@@ -34,4 +38,4 @@ print, closed forms, special cases and brute force; none is "parity
 unpinned".
 """
 
-from . import block_manager, fp8, paged_attention, sizes  # noqa: F401
+from . import block_manager, block_ops, fp8, paged_attention, sizes  # noqa: F401
