@@ -199,6 +199,45 @@ int pa_chunked_prefill(void* out, const void* query, const void* k_cache,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Whole-block copies.  Copy-on-write copies a shared block into a fresh one
+ * before a sequence writes into it ("03 -- PagedAttention & the vLLM V1
+ * Architecture", section "The block table walkthrough"; "High-Throughput
+ * Local LLM Infrastructure ...", section "Reference Counting &
+ * Copy-on-Write (CoW)"); preemption by swapping moves a sequence's blocks to
+ * pinned host memory and back ("03 -- ...", section "Preemption &
+ * eviction"; "Inside vLLM ...", section "Preemption Mechanics: Swapping vs.
+ * Recomputation").
+ *
+ * A pool is num_blocks blocks of block_bytes bytes, block b at
+ * pool + b * block_bytes: a K or V pool (block_bytes = num_kv_heads *
+ * block_size * head_dim * element size) or the scale array of an fp8 cache
+ * (block_bytes = 4 * num_kv_heads).  block_bytes must be a positive
+ * multiple of 4.  block_mapping is a device int64 array [num_pairs, 2] of
+ * (src, dst) block ids; block dst of the destination pool becomes a bit
+ * copy of block src of the source pool.  Destinations must be distinct, and
+ * for pa_copy_blocks no destination may also be a source of the same call
+ * (PA_ERR_INDEX under PA_CHECK=1, with ids out of range; without it such
+ * pairs are undefined, and out-of-range pairs are skipped).
+ * ---------------------------------------------------------------------- */
+
+/* pa_copy_blocks -- copies inside one device pool (copy-on-write). */
+int pa_copy_blocks(void* pool, const int64_t* block_mapping,
+                   int32_t num_pairs, int64_t block_bytes,
+                   int32_t num_blocks, void* stream);
+
+/*
+ * pa_swap_blocks -- copies from one pool into another; either may be pinned
+ * host memory (hipHostMalloc or a pinned torch tensor: the swap space) or
+ * device memory.  Pageable host memory returns PA_ERR_UNSUPPORTED before
+ * anything is launched.  dst_pool == src_pool returns PA_ERR_SHAPE (use
+ * pa_copy_blocks).
+ */
+int pa_swap_blocks(void* dst_pool, const void* src_pool,
+                   const int64_t* block_mapping, int32_t num_pairs,
+                   int64_t block_bytes, int32_t dst_num_blocks,
+                   int32_t src_num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
  * FP8 (e4m3) KV cache.  The cache may hold K and V as 8-bit floats, one
  * byte per element, quantised per block ("Tech Radar: vLLM v1 Production
  * Engine Architecture ...", section "Hopper TMA Warp Specialization & FP8

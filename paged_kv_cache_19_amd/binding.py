@@ -39,6 +39,8 @@ SIGNATURES = {
     "pa_chunked_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _i32, _vp, _sz, _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i32, ctypes.c_int64, _i32, _vp]),
+    "pa_swap_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.c_int64, _i32, _i32, _vp]),
     "pa_reshape_and_cache_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                 _i32, _i32, _i32, _vp]),
     "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -193,6 +195,40 @@ def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
         max_query_len, Hq, Hkv, D, B, NB, scale, _dtype(query), kv_split_tokens,
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+# -- whole-block copies ---------------------------------------------------------
+
+def _pool_ptr(t: torch.Tensor):
+    """Data pointer of a pool: a device tensor or a pinned host tensor."""
+    if not t.is_contiguous():
+        raise ValueError("libpa takes contiguous tensors")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError("a host pool must be pinned memory")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _block_bytes(pool: torch.Tensor) -> int:
+    return pool[0].numel() * pool.element_size()
+
+
+def copy_blocks(pool: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy-on-write inside one pool: block d = block s for every (s, d) row
+    of the device int64 ``block_mapping`` [n, 2]."""
+    _check("pa_copy_blocks", lib().pa_copy_blocks(
+        _ptr(pool), _ptr(block_mapping), block_mapping.shape[0], _block_bytes(pool),
+        pool.shape[0], _stream(stream)))
+
+
+def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor, block_mapping: torch.Tensor,
+                stream=None) -> None:
+    """Copy blocks between pools (device or pinned host): block d of
+    ``dst_pool`` = block s of ``src_pool`` for every (s, d) row."""
+    if _block_bytes(dst_pool) != _block_bytes(src_pool):
+        raise ValueError("pools with different block sizes")
+    _check("pa_swap_blocks", lib().pa_swap_blocks(
+        _pool_ptr(dst_pool), _pool_ptr(src_pool), _ptr(block_mapping), block_mapping.shape[0],
+        _block_bytes(dst_pool), dst_pool.shape[0], src_pool.shape[0], _stream(stream)))
 
 
 # -- FP8 (e4m3) KV cache -------------------------------------------------------

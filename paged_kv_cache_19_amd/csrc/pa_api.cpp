@@ -401,6 +401,97 @@ int pa_chunked_prefill(void* out, const void* query, const void* k_cache, const 
                           workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Device-accessible address of a pool: device memory as is, pinned host
+// memory through its mapped device pointer.  Pageable host memory (or any
+// pointer HIP does not know) is refused.
+int device_address(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the error for the next call
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = p;
+    return PA_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    const char* host = static_cast<const char*>(attr.hostPointer ? attr.hostPointer : p);
+    *out = static_cast<const char*>(attr.devicePointer) + (static_cast<const char*>(p) - host);
+    return PA_OK;
+  }
+  return PA_ERR_UNSUPPORTED;
+}
+
+// PA_CHECK for block mappings: ids in range, destinations distinct, and
+// within one pool no destination is also a source.
+int validate_mapping(const int64_t* d_map, int num_pairs, int64_t src_nb, int64_t dst_nb,
+                     bool same_pool, hipStream_t st) {
+  std::vector<int64_t> m(2 * (size_t)num_pairs);
+  if (hipMemcpyAsync(m.data(), d_map, m.size() * 8, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  std::vector<int64_t> dsts, srcs;
+  for (int p = 0; p < num_pairs; ++p) {
+    const int64_t s = m[2 * (size_t)p], d = m[2 * (size_t)p + 1];
+    if (s < 0 || s >= src_nb || d < 0 || d >= dst_nb) return PA_ERR_INDEX;
+    srcs.push_back(s);
+    dsts.push_back(d);
+  }
+  std::sort(dsts.begin(), dsts.end());
+  for (size_t i = 1; i < dsts.size(); ++i)
+    if (dsts[i] == dsts[i - 1]) return PA_ERR_INDEX;
+  if (same_pool)
+    for (int64_t s : srcs)
+      if (std::binary_search(dsts.begin(), dsts.end(), s)) return PA_ERR_INDEX;
+  return PA_OK;
+}
+
+int copy_common(void* dst, const void* src, const int64_t* mapping, int32_t num_pairs,
+                int64_t block_bytes, int32_t dst_num_blocks, int32_t src_num_blocks,
+                bool same_pool, void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 4 != 0 || dst_num_blocks <= 0 ||
+      src_num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst || !src || !mapping) return PA_ERR_NULL;
+  const void* dd = nullptr;
+  const void* sd = nullptr;
+  int rc = device_address(dst, &dd);
+  if (rc == PA_OK) rc = device_address(src, &sd);
+  if (rc != PA_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    rc = validate_mapping(mapping, num_pairs, src_num_blocks, dst_num_blocks, same_pool, st);
+    if (rc != PA_OK) return rc;
+  }
+  return pa::launch_copy_blocks(const_cast<void*>(dd), sd, mapping, num_pairs, block_bytes,
+                                src_num_blocks, dst_num_blocks, st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_copy_blocks(void* pool, const int64_t* block_mapping, int32_t num_pairs,
+                   int64_t block_bytes, int32_t num_blocks, void* stream) {
+  return copy_common(pool, pool, block_mapping, num_pairs, block_bytes, num_blocks, num_blocks,
+                     true, stream);
+}
+
+int pa_swap_blocks(void* dst_pool, const void* src_pool, const int64_t* block_mapping,
+                   int32_t num_pairs, int64_t block_bytes, int32_t dst_num_blocks,
+                   int32_t src_num_blocks, void* stream) {
+  if (dst_pool == src_pool && dst_pool != nullptr) return PA_ERR_SHAPE;  // use pa_copy_blocks
+  return copy_common(dst_pool, src_pool, block_mapping, num_pairs, block_bytes, dst_num_blocks,
+                     src_num_blocks, false, stream);
+}
+
 int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
                              const float* k_scales, const float* v_scales,
                              const int64_t* slot_mapping, int32_t num_tokens,

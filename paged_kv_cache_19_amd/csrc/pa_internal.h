@@ -54,6 +54,13 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int32_t num_blocks, int32_t elem_bytes,
                                     hipStream_t stream);
 
+// Copy whole blocks of block_bytes bytes (a multiple of 4): block dst of
+// ``dst`` becomes block src of ``src`` for each (src, dst) pair.  Both pools
+// are device-accessible addresses.
+hipError_t launch_copy_blocks(void* dst, const void* src, const int64_t* mapping,
+                              int32_t num_pairs, int64_t block_bytes, int64_t src_num_blocks,
+                              int64_t dst_num_blocks, hipStream_t stream);
+
 // Cache write into e4m3 pools (bf16 K/V in), quantised with the scale of
 // each slot's (block, KV head).
 hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_internal.h"
@@ -168,6 +169,31 @@ __global__ __launch_bounds__(16 * D * ES / 16) void reshape_and_cache_kernel(
         for (int e = 0; e < VEC; ++e) dst[(int64_t)e * B] = vals[e];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole-block copies between two pools (or inside one): copy-on-write and
+// swapping to / from pinned host memory.  Grid: x = chunks of one block,
+// y = mapping pairs (grid-stride); 16-byte accesses when the block size and
+// both pools allow, 4-byte ones otherwise.  Pairs naming a block outside a
+// pool are skipped.
+// ---------------------------------------------------------------------------
+template <typename V>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+    const int64_t* __restrict__ mapping, int num_pairs, int64_t block_bytes, int64_t src_nb,
+    int64_t dst_nb) {
+  const int64_t n = block_bytes / (int64_t)sizeof(V);
+  for (int p = blockIdx.y; p < num_pairs; p += gridDim.y) {
+    const int64_t sb = mapping[2 * (int64_t)p];
+    const int64_t db = mapping[2 * (int64_t)p + 1];
+    if (sb < 0 || sb >= src_nb || db < 0 || db >= dst_nb) continue;
+    const V* s = reinterpret_cast<const V*>(src + sb * block_bytes);
+    V* d = reinterpret_cast<V*>(dst + db * block_bytes);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+      d[i] = s[i];
   }
 }
 
@@ -1666,6 +1692,27 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   else if (elem_bytes == 4 && head_dim == 128) PA_RC(4, 128);
   else PA_RC(4, 64);
 #undef PA_RC
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* dst, const void* src, const int64_t* mapping,
+                              int32_t num_pairs, int64_t block_bytes, int64_t src_num_blocks,
+                              int64_t dst_num_blocks, hipStream_t stream) {
+  const bool v16 = block_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(dst) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(src) % 16 == 0;
+  const int64_t elems = block_bytes / (v16 ? 16 : 4);
+  const unsigned gx = (unsigned)std::min<int64_t>((elems + 255) / 256, 64);
+  const unsigned gy = (unsigned)std::min<int32_t>(num_pairs, 65535);
+  uint8_t* d = static_cast<uint8_t*>(dst);
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  if (v16)
+    copy_blocks_kernel<u32x4><<<dim3(gx, gy), 256, 0, stream>>>(d, s, mapping, num_pairs,
+                                                               block_bytes, src_num_blocks,
+                                                               dst_num_blocks);
+  else
+    copy_blocks_kernel<uint32_t><<<dim3(gx, gy), 256, 0, stream>>>(d, s, mapping, num_pairs,
+                                                                  block_bytes, src_num_blocks,
+                                                                  dst_num_blocks);
   return hipGetLastError();
 }
 

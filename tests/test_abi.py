@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding.SIGNATURES)
@@ -122,3 +122,17 @@ def test_binding_refuses_host_tensors(lib):
     t = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         binding.compute_slot_mapping(t.view(2, 2), t[:2], None, 16)
+
+
+def test_block_copy_entry_points_reject_bad_arguments(lib):
+    m = FAKE
+    assert lib.pa_copy_blocks(FAKE, m, 0, 64, 8, None) == 0           # nothing to do
+    assert lib.pa_copy_blocks(FAKE, m, 2, 0, 8, None) == -2           # block_bytes 0
+    assert lib.pa_copy_blocks(FAKE, m, 2, 6, 8, None) == -2           # not a multiple of 4
+    assert lib.pa_copy_blocks(FAKE, m, -1, 64, 8, None) == -2
+    assert lib.pa_copy_blocks(FAKE, m, 2, 64, 0, None) == -2
+    assert lib.pa_copy_blocks(None, m, 2, 64, 8, None) == -1
+    assert lib.pa_copy_blocks(FAKE, None, 2, 64, 8, None) == -1
+    assert lib.pa_swap_blocks(FAKE, FAKE, m, 2, 64, 8, 8, None) == -2   # same pool: use copy
+    assert lib.pa_swap_blocks(None, FAKE, m, 2, 64, 8, 8, None) == -1
+    assert lib.pa_swap_blocks(FAKE, ctypes.c_void_p(32), m, 2, 64, 8, 0, None) == -2
