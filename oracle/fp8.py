@@ -38,7 +38,7 @@ import math
 
 import torch
 
-from .paged_attention import _as_cpu_long, paged_attention
+from .paged_attention import _as_cpu_long, attention, gather_kv
 
 E4M3_MAX = 448.0
 
@@ -117,13 +117,42 @@ def dequantize_pool(cache: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
     return vals * s
 
 
+def gather_dequantized(k_cache, v_cache, k_scales, v_scales, table_row, length):
+    """Positions 0..length-1 of one sequence as float64 ``[L, H_kv, D]``:
+    the codes gathered through the table, times their block's scale."""
+    B = k_cache.shape[2]
+    K8, V8 = gather_kv(k_cache, v_cache, table_row, length)
+    pos = torch.arange(length)
+    blocks = _as_cpu_long(table_row)[pos // B]
+    table = decode_table()
+    K = table[K8.to(torch.int64)] * k_scales.to(torch.float64)[blocks][:, :, None]
+    V = table[V8.to(torch.int64)] * v_scales.to(torch.float64)[blocks][:, :, None]
+    return K, V
+
+
 def paged_attention_fp8(q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
                         query_start_loc, scale, seq_ids=None, rows=None) -> torch.Tensor:
-    """Paged attention over the dequantised pools (float64)."""
-    kd = dequantize_pool(k_cache, k_scales)
-    vd = dequantize_pool(v_cache, v_scales)
-    return paged_attention(q, kd, vd, block_tables, seq_lens, query_start_loc, scale,
-                           seq_ids=seq_ids, rows=rows)
+    """Paged attention over the dequantised values (float64); rows and
+    sequences are chosen as in ``paged_attention`` (others stay NaN).  Each
+    sequence is dequantised after its gather, which is the same arithmetic
+    as dequantising the whole pools first."""
+    lens = _as_cpu_long(seq_lens)
+    S = lens.numel()
+    qsl = (torch.arange(S + 1) if query_start_loc is None
+           else _as_cpu_long(query_start_loc))
+    bt = _as_cpu_long(block_tables)
+    out = torch.full(tuple(q.shape), math.nan, dtype=torch.float64)
+    wanted = None if rows is None else set(int(r) for r in rows)
+    for s in (range(S) if seq_ids is None else seq_ids):
+        r0, r1 = int(qsl[s]), int(qsl[s + 1])
+        L = int(lens[s])
+        picked = [r for r in range(r0, r1) if wanted is None or r in wanted]
+        if not picked:
+            continue
+        K, V = gather_dequantized(k_cache, v_cache, k_scales, v_scales, bt[s], L)
+        positions = [L - (r1 - r0) + (r - r0) for r in picked]
+        out[picked] = attention(q[picked], K, V, positions, scale)
+    return out
 
 
 def decode_fp8(q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, scale,

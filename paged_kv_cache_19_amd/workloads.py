@@ -28,6 +28,10 @@ Workload shapes (one attention layer; "G" = query heads per KV head):
 5. chunked prefill + decode mix, bf16: 4 requests with a 512-token query
    chunk after U[1024, 8192] cached tokens, then 60 decode sequences of
    U[256, 4096] tokens; 32/8 heads, head dim 128, block size 16.
+6. long-context decode, bf16: 8 sequences of U[32768, 131072] tokens at the
+   Llama-3-70B layer shape (64/8 heads, head dim 128, block size 16).
+7. Llama-3-70B layer decode with 32-token blocks: workload 3's batch shape
+   (128 sequences of U[2048, 8192] tokens, 64/8 heads) at block size 32.
 
 With ``kv_fp8`` the workload also carries an e4m3 KV cache: uint8 pools
 ``k_cache8`` / ``v_cache8`` (same layouts as the bf16 pools) of uniformly
@@ -71,6 +75,8 @@ SHAPES: Dict[int, Shape] = {
     3: Shape("llama3-70b-layer-decode-bf16", BF16, 64, 8, 128, 16),
     4: Shape("shared-prefix-decode-bf16", BF16, 32, 8, 128, 16),
     5: Shape("chunked-prefill-mix-bf16", BF16, 32, 8, 128, 16),
+    6: Shape("long-context-decode-bf16", BF16, 64, 8, 128, 16),
+    7: Shape("llama3-70b-layer-decode-b32-bf16", BF16, 64, 8, 128, 32),
 }
 
 
@@ -163,6 +169,12 @@ def _draw_lengths(cfg: int, rng: np.random.Generator):
         dec = rng.integers(256, 4096 + 1, size=60)
         lens = (ctx + 512).tolist() + dec.tolist()
         return lens, [512] * 4 + [1] * 60, 0
+    if cfg == 6:
+        lens = rng.integers(32768, 131072 + 1, size=8)
+        return lens.tolist(), [1] * 8, 0
+    if cfg == 7:
+        lens = rng.integers(2048, 8192 + 1, size=128)
+        return lens.tolist(), [1] * 128, 0
     raise ValueError(f"unknown workload {cfg}")
 
 
@@ -172,7 +184,7 @@ def make_workload(cfg: int, seed: Optional[int] = None, device: str = "cpu",
                   shape: Optional[Shape] = None,
                   shared_prefix_tokens: Optional[int] = None,
                   num_blocks: Optional[int] = None, kv_fp8: bool = False) -> Workload:
-    """Draw workload ``cfg`` (1..5) with ``seed`` (default 1000 + cfg).
+    """Draw workload ``cfg`` (1..7) with ``seed`` (default 1000 + cfg).
 
     ``seq_lens``/``q_lens``/``shape``/``shared_prefix_tokens``/``num_blocks``
     override the named workload to build custom cases (ragged tails, tiny

@@ -70,7 +70,7 @@ def _run_fp8(wl, max_seqs=None, refcounts=True, check_write=True):
     return out, err
 
 
-@pytest.mark.parametrize("cfg,max_seqs", [(2, None), (3, 10), (4, 16)])
+@pytest.mark.parametrize("cfg,max_seqs", [(2, None), (3, 10), (4, 16), (6, 4), (7, 10)])
 def test_fp8_workload_parity(cfg, max_seqs):
     log(f"[fp8] workload {cfg}")
     wl = workloads.make_workload(cfg, device="cuda", kv_fp8=True)

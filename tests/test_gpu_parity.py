@@ -17,10 +17,10 @@ from tests.gpu_common import TOL, log, run_and_compare
 
 pytestmark = pytest.mark.gpu
 
-FULL_SIZE_SEQ_SAMPLE = {1: None, 2: None, 3: 12, 4: 16, 5: None}
+FULL_SIZE_SEQ_SAMPLE = {1: None, 2: None, 3: 12, 4: 16, 5: None, 6: 4, 7: 12}
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7])
 def test_workload_parity(cfg):
     log(f"[parity] workload {cfg}: {workloads.SHAPES[cfg].name}")
     wl = workloads.make_workload(cfg, device="cuda")

@@ -182,16 +182,19 @@ def _quantize_multiply(x, scale):
     return f8.encode(y).reshape(x.shape)
 
 
-def _dequantize_wrong_block(cache, scales):
-    vals = f8.decode_table()[cache.to(torch.int64)]
-    return vals * scales.roll(1, 0).to(torch.float64)[:, :, None, None]
+_orig_gather = f8.gather_dequantized
+
+
+def _gather_wrong_block_scale(k_cache, v_cache, k_scales, v_scales, table_row, length):
+    return _orig_gather(k_cache, v_cache, k_scales.roll(1, 0), v_scales.roll(1, 0),
+                        table_row, length)
 
 
 @pytest.mark.parametrize("name,fn", [
     ("encode", _encode_ties_away),
     ("quantize", _quantize_no_clamp),
     ("quantize", _quantize_multiply),
-    ("dequantize_pool", _dequantize_wrong_block),
+    ("gather_dequantized", _gather_wrong_block_scale),
 ])
 def test_planted_fp8_mistake_fails_a_pin(monkeypatch, name, fn):
     monkeypatch.setattr(f8, name, fn)
@@ -212,3 +215,22 @@ def test_planted_v_scale_mistake_fails_brute_force(monkeypatch):
         return orig(k_cache, v_cache, k_scales, k_scales, key, value, slot_mapping)
     monkeypatch.setattr(f8, "reshape_and_cache_fp8", bad)
     assert not _fp8_pins_pass()
+
+
+def test_per_sequence_dequantisation_equals_whole_pool_dequantisation():
+    """The oracle dequantises each gathered sequence; the plain reading
+    dequantises the whole pools and runs ``paged_attention`` on them."""
+    from oracle import paged_attention as pa
+    g = torch.Generator().manual_seed(12)
+    NB, H, B, D = 9, 2, 4, 8
+    kc = torch.randint(0, 126, (NB, H, B, D), generator=g).to(torch.uint8)
+    vc = torch.randint(128, 254, (NB, H, D, B), generator=g).to(torch.uint8)
+    ks = torch.rand(NB, H, generator=g) * 0.1 + 0.01
+    vs = torch.rand(NB, H, generator=g) * 0.1 + 0.01
+    bt = torch.tensor([[4, 1, 7], [2, 8, 0]])
+    lens, qsl = [11, 6], [0, 3, 4]
+    q = torch.randn(4, 4, D, generator=g, dtype=torch.float64)
+    got = f8.paged_attention_fp8(q, kc, vc, ks, vs, bt, lens, qsl, 0.4)
+    want = pa.paged_attention(q, f8.dequantize_pool(kc, ks), f8.dequantize_pool(vc, vs), bt,
+                              lens, qsl, 0.4)
+    assert torch.allclose(got, want, rtol=0, atol=1e-13)
