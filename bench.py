@@ -1,20 +1,27 @@
 #!/usr/bin/env python3
-"""Paged-attention decode benchmark on one MI355X.
+"""Paged-attention benchmark on one MI355X.
 
-One step = the whole hot path over one synthetic decode batch, through the C
-ABI: slot mapping for the new tokens, the cache write of their K/V, and
-split-K paged decode attention (attention pass + log-sum-exp merge).  Inputs
-are resident in HBM before the timed region.
+One step = the whole hot path over one synthetic batch, through the C ABI:
+slot mapping for the new tokens, the cache write of their K/V, and paged
+attention (pa_decode, or pa_chunked_prefill for the prefill + decode mix).
+Inputs are resident in HBM before the timed region.
 
-Workload (default): one Llama-3-70B attention layer in bf16 -- 128 sequences
-of U[2048, 8192] tokens, 64 query / 8 KV heads, head_dim 128, block size 16,
-blocks scattered by a seeded permutation of the pool.
+Workload (default 3): one Llama-3-70B attention layer in bf16 -- 128
+sequences of U[2048, 8192] tokens, 64 query / 8 KV heads, head_dim 128,
+block size 16, blocks scattered by a seeded permutation of the pool.
+``--workload`` picks another of the seeded workloads (2: Llama-3-8B layer,
+4: shared prefix, 5: chunked prefill + decode mix, 6: long context
+U[32K, 128K], 7: workload 3 with 32-token blocks); ``--kv-dtype fp8`` runs
+the decode workloads on the e4m3 cache (cache write and decode of the fp8
+entry points).
 
 Prints ONE JSON line.  ``value`` is the step's KV-read throughput in GB/s
 (algorithmic KV bytes / step time); tokens/s and the fraction of the 8 TB/s
-HBM peak ride along.  ``roofline`` covers pa_decode (the dominant call),
-timed with HIP events on the stream its kernels run on.  ``cpu_baseline`` is
-the CPU oracle timed on a bounded sample of the same batch.
+HBM peak ride along.  ``roofline`` covers the attention call (the dominant
+one), timed with HIP events on the stream its kernels run on: HBM-bound for
+decode, MFMA-bound (bf16 dense peak) for the chunked-prefill mix.
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
+batch.
 """
 from __future__ import annotations
 
@@ -30,8 +37,18 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attention decode KV-read GB/s (% of HBM peak) and tokens/s, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "paged_kv_cache_19_amd", "csrc")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_llama3-70b-layer_hbm_counters.md")
+
+SEQ_LENS = {
+    2: "U[512,4096]",
+    3: "U[2048,8192]",
+    4: "512 shared + U[64,1024]",
+    5: "4 x (ctx U[1024,8192] + 512-token chunk) + 60 decode U[256,4096]",
+    6: "U[32768,131072]",
+    7: "U[2048,8192]",
+}
 
 
 def kernel_source_digest() -> str:
@@ -44,11 +61,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: int):
+def measured_traffic(workload: int, kv_dtype: str):
     """HBM bytes per pa_decode call from the committed rocprofv3 counter
     summary, or None when the summary is missing, is for another workload, or
     was taken on different kernel sources."""
-    if workload != 3 or not os.path.exists(PMC_SUMMARY):
+    if workload != 3 or kv_dtype != "bf16" or not os.path.exists(PMC_SUMMARY):
         return None
     fields = {}
     with open(PMC_SUMMARY) as f:
@@ -69,7 +86,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    p.add_argument("--workload", type=int, default=3, choices=sorted(SEQ_LENS))
+    p.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"])
     p.add_argument("--kv-split", type=int, default=0, help="keys per split (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -80,52 +98,92 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(wl):
-    """Bytes pa_decode must move: every sequence's K and V (token-exact),
-    the query and output rows, the block-table entries it reads and seq_lens.
-    For a shared prefix the shared blocks count once (unique bytes)."""
+def kv_bytes_per_token(shp, kv_dtype):
+    e = 1 if kv_dtype == "fp8" else (2 if shp.dtype == "bf16" else 4)
+    return 2 * shp.num_kv_heads * shp.head_dim * e
+
+
+def algorithmic_bytes(wl, kv_dtype="bf16"):
+    """Bytes the attention call must move: every sequence's K and V
+    (token-exact), the query and output rows, the block-table entries it
+    reads and seq_lens (and, for fp8, one K and one V scale per block and KV
+    head).  For a shared prefix the shared blocks count once (unique
+    bytes).  Returns (KV bytes, all bytes)."""
     shp = wl.shape
     e = 2 if shp.dtype == "bf16" else 4
-    per_tok = 2 * shp.num_kv_heads * shp.head_dim * e
     shared_tokens = len(wl.shared_blocks) * shp.block_size
     kv_tokens = sum(wl.seq_lens) - shared_tokens * (wl.num_seqs - 1)
-    kv = kv_tokens * per_tok
+    kv = kv_tokens * kv_bytes_per_token(shp, kv_dtype)
     qo = 2 * wl.num_tokens * shp.num_q_heads * shp.head_dim * e
-    tables = sum(-(-L // shp.block_size) for L in wl.seq_lens) * 4 + wl.num_seqs * 4
-    return kv, kv + qo + tables
+    nblk = sum(-(-L // shp.block_size) for L in wl.seq_lens)
+    tables = nblk * 4 + wl.num_seqs * 4
+    scales = nblk * shp.num_kv_heads * 8 if kv_dtype == "fp8" else 0
+    return kv, kv + qo + tables + scales
 
 
-def cpu_baseline(wl, budget_s):
+def algorithmic_flops(wl):
+    """4 * H_q * D flops (QK^T and PV multiply-adds) per key each query row
+    attends to (causal: row j of a q_len chunk sees L - q_len + j + 1 keys).
+    Returns (query-chunk flops, single-row flops)."""
+    shp = wl.shape
+    chunk = single = 0
+    for L, n in zip(wl.seq_lens, wl.q_lens):
+        keys = n * (L - n) + n * (n + 1) // 2
+        f = 4 * shp.num_q_heads * shp.head_dim * keys
+        if n > 1:
+            chunk += f
+        else:
+            single += f
+    return chunk, single
+
+
+def cpu_baseline(wl, budget_s, kv_dtype):
     """The oracle (gather through the block table + float64 softmax attention)
     on whole sequences of the same batch, cycling through it until about
     ``budget_s`` seconds of CPU work are done."""
     import torch
 
     import oracle.paged_attention as ref
+    import oracle.fp8 as ref8
 
-    kc = wl.tensors["k_cache"].cpu()
-    vc = wl.tensors["v_cache"].cpu()
-    q = wl.tensors["query"].cpu()
+    t = wl.tensors
+    q = t["query"].cpu()
     bt = wl.block_tables_tensor("cpu")
-    n_seqs, n_tok, kv_bytes = 0, 0, 0
-    per_tok = 2 * wl.shape.num_kv_heads * wl.shape.head_dim * 2
+    qsl = wl.query_start_loc()
+    if kv_dtype == "fp8":
+        pools = (t["k_cache8"].cpu(), t["v_cache8"].cpu(), t["k_scales"].cpu(),
+                 t["v_scales"].cpu())
+    else:
+        pools = (t["k_cache"].cpu(), t["v_cache"].cpu())
+    n_seqs = n_rows = n_tok = kv_bytes = 0
+    per_tok = kv_bytes_per_token(wl.shape, kv_dtype)
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         s = n_seqs % wl.num_seqs
-        ref.decode(q, kc, vc, bt, wl.seq_lens, wl.scale, seq_ids=[s])
+        if kv_dtype == "fp8":
+            ref8.paged_attention_fp8(q, *pools, bt, wl.seq_lens, qsl, wl.scale, seq_ids=[s])
+        else:
+            ref.paged_attention(q, *pools, bt, wl.seq_lens, qsl, wl.scale, seq_ids=[s])
         n_seqs += 1
+        n_rows += wl.q_lens[s]
         n_tok += wl.seq_lens[s]
         kv_bytes += wl.seq_lens[s] * per_tok
     dt = time.perf_counter() - t0
     return {
-        "value": round(n_seqs / dt, 3),
+        "value": round(n_rows / dt, 3),
         "unit": "tokens/s",
         "kv_gbs": round(kv_bytes / dt / 1e9, 4),
         "cores": torch.get_num_threads(),
         "kind": "oracle",
-        "sample": f"{n_seqs} decode rows (sequences of the same batch, cycled; {n_tok} cached "
-                  f"tokens, all 64 heads each) in {dt:.1f} s",
+        "sample": f"{n_seqs} sequences of the same batch (cycled; {n_rows} query rows, {n_tok} "
+                  f"cached tokens, all {wl.shape.num_q_heads} heads each) in {dt:.1f} s",
     }
+
+
+def percentile(xs, p):
+    xs = sorted(xs)
+    k = min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))
+    return xs[k]
 
 
 def main():
@@ -133,6 +191,11 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    fp8 = args.kv_dtype == "fp8"
+    if fp8 and (args.workload == 5 or args.kv_split):
+        print("the fp8 cache runs the balanced decode only (no chunked prefill, no fixed "
+              "split)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -142,27 +205,54 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()  # raises if libpa.so is missing
     dev = "cuda"
-    wl = workloads.make_workload(args.workload, device=dev)
+    wl = workloads.make_workload(args.workload, device=dev, kv_fp8=fp8)
     shp = wl.shape
     t = wl.tensors
     bt = wl.block_tables_tensor(dev)
     lens = wl.seq_lens_tensor(dev)
     refcounts = wl.block_refcounts_tensor(dev)
-    S, Hq, D = t["query"].shape
-    ws = torch.zeros(binding.decode_workspace_bytes(S, Hq, D, wl.max_seq_len, shp.block_size,
-                                                    args.kv_split), dtype=torch.uint8, device=dev)
+    chunked = args.workload == 5
+    qsl = wl.query_start_loc_tensor(dev) if chunked else None
+    T, Hq, D = t["query"].shape
+    S = wl.num_seqs
+    if chunked:
+        ws_bytes = binding.chunked_prefill_workspace_bytes(S, T, Hq, D, wl.max_seq_len,
+                                                           shp.block_size, args.kv_split)
+    elif fp8:
+        ws_bytes = binding.decode_fp8_workspace_bytes(S, Hq, D, wl.max_seq_len, shp.block_size)
+    else:
+        ws_bytes = binding.decode_workspace_bytes(S, Hq, D, wl.max_seq_len, shp.block_size,
+                                                  args.kv_split)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["query"])
-    slots = torch.empty(S, dtype=torch.int64, device=dev)
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
 
+    def attention():
+        if chunked:
+            binding.chunked_prefill(t["query"], t["k_cache"], t["v_cache"], bt, lens, qsl,
+                                    wl.max_seq_len, wl.max_query_len, wl.scale,
+                                    kv_split_tokens=args.kv_split, block_refcounts=refcounts,
+                                    out=out, workspace=ws)
+        elif fp8:
+            binding.decode_fp8(t["query"], t["k_cache8"], t["v_cache8"], t["k_scales"],
+                               t["v_scales"], bt, lens, wl.max_seq_len, wl.scale,
+                               block_refcounts=refcounts, out=out, workspace=ws)
+        else:
+            binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len,
+                           wl.scale, kv_split_tokens=args.kv_split, block_refcounts=refcounts,
+                           out=out, workspace=ws)
+
     def step(ev=None):
-        binding.compute_slot_mapping(bt, lens, None, shp.block_size, out=slots)
-        binding.reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], slots)
+        binding.compute_slot_mapping(bt, lens, qsl, shp.block_size, num_tokens=T, out=slots)
+        if fp8:
+            binding.reshape_and_cache_fp8(t["key"], t["value"], t["k_cache8"], t["v_cache8"],
+                                          t["k_scales"], t["v_scales"], slots)
+        else:
+            binding.reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], slots)
         if ev is not None:
             ev[0].record(stream)
-        binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len, wl.scale,
-                       kv_split_tokens=args.kv_split, block_refcounts=refcounts, out=out,
-                       workspace=ws)
+        attention()
         if ev is not None:
             ev[1].record(stream)
 
@@ -189,15 +279,47 @@ def main():
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    decode_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    decode_avg = sum(decode_ms) / len(decode_ms)
-    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, pa_decode avg "
-          f"{decode_avg:.4f} ms (min {decode_ms[0]:.4f}, max {decode_ms[-1]:.4f})",
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    call = "pa_chunked_prefill" if chunked else ("pa_decode_fp8" if fp8 else "pa_decode")
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, {call} avg "
+          f"{attn_avg:.4f} ms (p10 {percentile(attn_ms, 10):.4f}, median "
+          f"{percentile(attn_ms, 50):.4f}, p90 {percentile(attn_ms, 90):.4f})",
           file=sys.stderr, flush=True)
 
-    kv_bytes, decode_bytes = algorithmic_bytes(wl)
+    kv_bytes, call_bytes = algorithmic_bytes(wl, args.kv_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = decode_bytes / (decode_avg * 1e-3) / 1e9
+    if chunked:
+        f_chunk, f_single = algorithmic_flops(wl)
+        achieved = (f_chunk + f_single) / (attn_avg * 1e-3) / 1e12
+        roofline = {
+            "kernel": "pa_chunked_prefill: persistent query-chunk kernel (MFMA) + balanced "
+                      "decode of the single-token rows + merges",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": f_chunk + f_single,
+            "avg_launch_ms": round(attn_avg, 5),
+            "traffic": None,
+        }
+    else:
+        achieved = call_bytes / (attn_avg * 1e-3) / 1e9
+        roofline = {
+            "kernel": f"{call}: balanced split-K attention kernel + merge kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": call_bytes,
+            "avg_launch_ms": round(attn_avg, 5),
+            "traffic": measured_traffic(args.workload, args.kv_dtype),
+        }
+    roofline["p10_ms"] = round(percentile(attn_ms, 10), 5)
+    roofline["median_ms"] = round(percentile(attn_ms, 50), 5)
+    roofline["p90_ms"] = round(percentile(attn_ms, 90), 5)
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -209,40 +331,31 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": shp.dtype,
+        "dtype": "fp8-e4m3 cache, bf16 q/out" if fp8 else shp.dtype,
         "data": "synthetic",
         "config": {
-            "workload": shp.name,
+            "workload": shp.name if not fp8 else shp.name.replace("-bf16", "-fp8kv"),
             "num_seqs": wl.num_seqs,
+            "num_query_tokens": T,
             "num_q_heads": shp.num_q_heads,
             "num_kv_heads": shp.num_kv_heads,
             "head_dim": shp.head_dim,
             "block_size": shp.block_size,
-            "seq_lens": {2: "U[512,4096]", 3: "U[2048,8192]", 4: "512 shared + U[64,1024]"}[
-                args.workload],
+            "kv_cache": args.kv_dtype,
+            "seq_lens": SEQ_LENS[args.workload],
             "seed": wl.seed,
             "total_tokens": sum(wl.seq_lens),
             "kv_bytes": kv_bytes,
             "kv_split_tokens": args.kv_split,
-            "step": "slot mapping + reshape_and_cache + pa_decode",
+            "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + {call}",
         },
-        "tokens_per_s": round(wl.num_seqs / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": {
-            "kernel": "pa_decode: balanced split-K attention kernel + merge kernel",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": decode_bytes,
-            "avg_launch_ms": round(decode_avg, 5),
-            "traffic": measured_traffic(args.workload),
-        },
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.kv_dtype)
     print(json.dumps(result), flush=True)
 
 
