@@ -29,6 +29,12 @@ What the oracle computes, and the passage each part follows:
   attention over the dequantised pools ("Tech Radar: vLLM v1 Production
   Engine Architecture ...", section "Hopper TMA Warp Specialization & FP8
   Kernel Integration", item "FP8 Block-Quantized Caching").
+* ``scheduler`` -- the host batch builder: the chunked-prefill token budget
+  ("Tech Radar: vLLM v1 ...", section "The Dynamic Chunked Prefill
+  Scheduler Formulation"), the schedule() step ("03 -- PagedAttention & the
+  vLLM V1 Architecture", section "The scheduler's schedule() step"),
+  hash-chained prefix reuse and preemption by recomputation; it emits the
+  tables, lengths, query offsets and slots the attention calls take.
 * ``sizes`` -- the closed forms for block counts, KV bytes and internal
   fragmentation ("Tech Radar: vLLM v1 Production Engine Architecture ...",
   section "Mathematical Modeling of PagedAttention v3 Memory Bounds").
@@ -38,4 +44,4 @@ print, closed forms, special cases and brute force; none is "parity
 unpinned".
 """
 
-from . import block_manager, block_ops, fp8, paged_attention, sizes  # noqa: F401
+from . import block_manager, block_ops, fp8, paged_attention, scheduler, sizes  # noqa: F401

@@ -1,0 +1,221 @@
+"""Pins of the host batch builder oracle (``oracle/scheduler.py``).
+
+* The chunked-prefill numbers of "Tech Radar: vLLM v1 ...", section "3.
+  Dynamic Chunked Prefill" (``tests/golden/chunked_prefill_schedule.json``):
+  64 decode streams, a 32K prompt, budget 2048, 1024-token chunks -> chunk 1
+  is tokens 0..1023 and the prompt takes 32 chunks; C_avail = 1984.
+* The block-table walkthrough of "03 -- PagedAttention & the vLLM V1
+  Architecture" reached through prefix reuse instead of fork: the end state
+  (tables [0, 1, 3] / [0, 2, 4], block 0 shared with reference count 2) is
+  the page's.
+* FNV-1a 64-bit against its published test vectors.
+* A fuzz run with token ids written into a simulated pool through the
+  emitted slots: every scheduled sequence reads back exactly its own tokens
+  through its table (prefix hits included), budgets hold, invariants hold.
+Planted mistakes (budget not reduced by decode rows, a hit on a partial
+block, a wrong slot offset) fail.
+"""
+import json
+import os
+import random
+
+import pytest
+
+import oracle.scheduler as sch
+from tests.conftest import GOLDEN
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_fnv1a64_published_vectors():
+    assert sch.fnv1a64(b"") == 0xCBF29CE484222325
+    assert sch.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert sch.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def _sample(req_id, pos):
+    return (req_id * 7919 + pos * 104729 + 13) % 32000
+
+
+def run(s, steps, pool=None, B=None, check=True):
+    """Drive ``steps`` steps; with ``pool`` (dict slot -> (req, pos, token)),
+    write token ids through the slots and check reads through tables."""
+    out = []
+    for _ in range(steps):
+        batch = s.step()
+        out.append(batch)
+        by_id = {r.req_id: r for r in s.running}
+        for e in batch.entries:
+            r = by_id[e.req_id]
+            first = e.seq_len - e.q_len
+            if pool is not None:
+                for j, slot in enumerate(e.slots):
+                    pool[slot] = r.tokens[first + j]
+                for p in range(e.seq_len):
+                    blk = e.table[p // B]
+                    assert pool.get(blk * B + p % B) == r.tokens[p], (e.req_id, p)
+        sampled = {e.req_id: _sample(e.req_id, e.seq_len) for e in batch.entries}
+        s.update(batch, sampled)
+        if check:
+            s.check_invariants()
+    return out
+
+
+def test_chunk_formula_worked_example():
+    g = _load("chunked_prefill_schedule.json")
+    n_dec, budget, chunk = g["decode_streams"], g["token_budget"], g["chunk_tokens"]
+    s = sch.Scheduler(num_blocks=4096, block_size=16, token_budget=budget, chunk_tokens=chunk)
+    for i in range(n_dec):
+        s.add_request(i, [i + 1], max_new_tokens=1000)
+    run(s, 1)                                         # the 64 one-token prompts
+    s.add_request(999, list(range(g["prompt_tokens"])), max_new_tokens=4)
+    chunks = []
+    for _ in range(g["num_chunks"] + 2):
+        batch = run(s, 1)[0]
+        dec = [e for e in batch.entries if e.q_len == 1 and e.req_id != 999]
+        assert len(dec) == n_dec                       # every decode stream served first
+        pre = [e for e in batch.entries if e.req_id == 999]
+        if pre and pre[0].q_len > 1:
+            chunks.append((pre[0].seq_len - pre[0].q_len, pre[0].seq_len - 1))
+            assert sum(e.q_len for e in batch.entries) <= budget
+    assert chunks[0] == tuple(g["first_chunk"])
+    assert len(chunks) == g["num_chunks"]
+    assert chunks[-1][1] == g["prompt_tokens"] - 1
+    # equation 3 with C_chunk above C_avail: the chunk is C_avail
+    s2 = sch.Scheduler(4096, 16, budget, 2048)
+    for i in range(n_dec):
+        s2.add_request(i, [i + 1], max_new_tokens=1000)
+    run(s2, 1)
+    s2.add_request(999, list(range(g["prompt_tokens"])), max_new_tokens=4)
+    e = [e for e in run(s2, 1)[0].entries if e.req_id == 999][0]
+    assert e.q_len == g["c_avail"]
+
+
+def test_walkthrough_reached_by_prefix_reuse():
+    g = _load("walkthrough.json")
+    B = g["block_size"]
+    s = sch.Scheduler(num_blocks=16, block_size=B, token_budget=64, chunk_tokens=64)
+    shared = [101, 102, 103, 104, 105, 106]            # the six tokens both agree on
+    a_tokens = shared + [7]                            # A's prompt reaches position 6 ("and")
+    s.add_request(0, a_tokens, max_new_tokens=100)
+    sampled_a = iter([8, 9, 10, 11, 12])
+    sampled_b = iter([70, 71, 72, 73])                 # B diverges at position 6 ("but")
+    pool = {}
+    for step in range(6):
+        if step == 1:
+            s.add_request(1, shared, max_new_tokens=100)
+        batch = s.step()
+        by_id = {r.req_id: r for r in s.running}
+        for e in batch.entries:
+            r = by_id[e.req_id]
+            for j, slot in enumerate(e.slots):
+                pool[slot] = r.tokens[e.seq_len - e.q_len + j]
+        s.update(batch, {0: next(sampled_a, 0), 1: next(sampled_b, 0)})
+        s.check_invariants()
+    A, Bq = (next(r for r in s.running if r.req_id == i) for i in (0, 1))
+    assert A.table == g["block_tables"]["A"] and Bq.table == g["block_tables"]["B"]
+    assert A.num_computed == g["seq_lens"]["A"] and Bq.num_computed == g["seq_lens"]["B"]
+    for entry in g["pool"]:
+        assert s.rc[entry["block"]] == entry["refcount"]
+    # block 0 holds the shared tokens once; B's own block 2 holds positions 4..7
+    assert [pool[p] for p in range(4)] == shared[:4]
+    assert [pool[2 * B + o] for o in range(4)] == Bq.tokens[4:8]
+
+
+def _fuzz(seed, steps=60, num_blocks=48, max_new=10):
+    rng = random.Random(seed)
+    B = 4
+    s = sch.Scheduler(num_blocks=num_blocks, block_size=B, token_budget=24, chunk_tokens=8,
+                      free_order=rng.sample(range(num_blocks), num_blocks))
+    prefixes = [[rng.randrange(50) for _ in range(rng.randrange(1, 14))] for _ in range(3)]
+    pool = {}
+    nid = 0
+    for _ in range(steps):
+        for _ in range(rng.randrange(0, 3)):
+            pre = rng.choice(prefixes) if rng.random() < 0.6 else []
+            prompt = pre + [rng.randrange(50) for _ in range(rng.randrange(1, 12))]
+            s.add_request(nid, prompt, max_new_tokens=rng.randrange(1, max_new))
+            nid += 1
+        batch = run(s, 1, pool, B)[0]
+        s.preemptions = getattr(s, "preemptions", 0) + len(batch.preempted)
+        n_dec = sum(1 for e in batch.entries if e.q_len == 1)
+        assert sum(e.q_len for e in batch.entries if e.q_len > 1) <= max(0, 24 - n_dec) + 0
+    return s
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_tokens_read_back_through_tables(seed):
+    _fuzz(seed)
+
+
+def test_fuzz_under_memory_pressure_preempts_and_recovers():
+    n = 0
+    for seed in range(6):
+        s = _fuzz(seed, steps=80, num_blocks=14, max_new=40)
+        n += s.preemptions
+    assert n > 0
+
+
+def test_fuzz_exercises_hits_and_preemption():
+    hits = preempts = 0
+    orig = sch.Scheduler._lookup
+
+    def counting(self, req):
+        nonlocal hits
+        h = orig(self, req)
+        hits += len(h)
+        return h
+    sch.Scheduler._lookup = counting
+    try:
+        for seed in range(6):
+            s = _fuzz(seed)
+    finally:
+        sch.Scheduler._lookup = orig
+    assert hits > 0
+
+
+def _bad_budget(self):
+    self.token_budget += 64          # decode rows not taken out of the budget
+    try:
+        return _orig_step(self)
+    finally:
+        self.token_budget -= 64
+
+
+def _bad_lookup(self, req):
+    hits = _orig_lookup(self, req)
+    if hits:
+        return hits
+    # a hit on the first block even when only part of it matches
+    parent = sch.FNV_OFFSET
+    for k, b in self.block_of_key.items():
+        return [(b, k)] if len(req.tokens) > self.B else []
+    return []
+
+
+def _bad_slots(self, req, c):
+    e = _orig_schedule(self, req, c)
+    e.slots = [x + 1 if i == 0 else x for i, x in enumerate(e.slots)]
+    return e
+
+
+_orig_step = sch.Scheduler.step
+_orig_lookup = sch.Scheduler._lookup
+_orig_schedule = sch.Scheduler._schedule
+
+
+@pytest.mark.parametrize("name,bad", [("step", _bad_budget), ("_lookup", _bad_lookup),
+                                      ("_schedule", _bad_slots)])
+def test_planted_scheduler_mistake_fails(monkeypatch, name, bad):
+    monkeypatch.setattr(sch.Scheduler, name, bad)
+    failed = False
+    try:
+        test_chunk_formula_worked_example()
+        for seed in range(6):
+            _fuzz(seed)
+    except (AssertionError, KeyError, IndexError):
+        failed = True
+    assert failed
