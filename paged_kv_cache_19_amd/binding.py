@@ -41,6 +41,14 @@ SIGNATURES = {
                                           _i32, _i32, _vp, _sz, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i32, ctypes.c_int64, _i32, _vp]),
     "pa_swap_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.c_int64, _i32, _i32, _vp]),
+    "pa_sched_create": (_vp, [_i32, _i32, _i32, _i32, _vp]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_add_request": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _i32, _i32]),
+    "pa_sched_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
+    "pa_sched_get_batch": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp]),
+    "pa_sched_update": (ctypes.c_int, [_vp, _vp, _vp, _i32]),
+    "pa_sched_block_refcounts": (ctypes.c_int, [_vp, _vp, _i32]),
+    "pa_sched_counts": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
     "pa_reshape_and_cache_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                 _i32, _i32, _i32, _vp]),
     "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -292,3 +300,80 @@ def decode_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         max_seq_len, Hq, Hkv, D, B, NB, scale, _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return out
+
+
+# -- host batch builder (include/pa_sched.h) ------------------------------------
+
+class BatchBuilder:
+    """The native batch builder: queue requests, schedule steps, feed back
+    sampled tokens.  Host memory only; arrays are numpy."""
+
+    def __init__(self, num_blocks: int, block_size: int, token_budget: int, chunk_tokens: int,
+                 free_order=None):
+        import numpy as np
+        self._np = np
+        fo = None
+        if free_order is not None:
+            fo = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+        self.num_blocks = num_blocks
+        self._h = lib().pa_sched_create(num_blocks, block_size, token_budget, chunk_tokens,
+                                        None if fo is None else fo.ctypes.data_as(ctypes.c_void_p))
+        if not self._h:
+            raise PAError("pa_sched_create", -2)
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_request(self, req_id: int, prompt, max_new_tokens: int) -> None:
+        p = self._np.ascontiguousarray(self._np.asarray(prompt, dtype=self._np.int32))
+        _check("pa_sched_add_request", lib().pa_sched_add_request(
+            self._h, req_id, p.ctypes.data_as(ctypes.c_void_p), p.size, max_new_tokens))
+
+    def step(self, pad_block: int = 0) -> dict:
+        np = self._np
+        n = [ctypes.c_int32() for _ in range(4)]
+        _check("pa_sched_step", lib().pa_sched_step(self._h, *[ctypes.byref(x) for x in n]))
+        S, T, MB, P = (x.value for x in n)
+        mb = max(MB, 1)
+        out = {
+            "req_ids": np.zeros(S, np.int64), "seq_lens": np.zeros(S, np.int32),
+            "query_start_loc": np.zeros(S + 1, np.int32),
+            "block_tables": np.zeros((S, mb), np.int32), "slot_mapping": np.zeros(T, np.int64),
+            "preempted": np.zeros(P, np.int64),
+        }
+
+        def ptr(a):
+            return a.ctypes.data_as(ctypes.c_void_p)
+        _check("pa_sched_get_batch", lib().pa_sched_get_batch(
+            self._h, ptr(out["req_ids"]), ptr(out["seq_lens"]), ptr(out["query_start_loc"]),
+            ptr(out["block_tables"]), mb, pad_block, ptr(out["slot_mapping"]),
+            ptr(out["preempted"]) if P else None))
+        return out
+
+    def update(self, sampled: dict) -> None:
+        np = self._np
+        ids = np.ascontiguousarray(np.fromiter(sampled.keys(), np.int64, len(sampled)))
+        toks = np.ascontiguousarray(np.fromiter(sampled.values(), np.int32, len(sampled)))
+        _check("pa_sched_update", lib().pa_sched_update(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), toks.ctypes.data_as(ctypes.c_void_p),
+            len(sampled)))
+
+    def block_refcounts(self):
+        out = self._np.zeros(self.num_blocks, self._np.int32)
+        _check("pa_sched_block_refcounts", lib().pa_sched_block_refcounts(
+            self._h, out.ctypes.data_as(ctypes.c_void_p), self.num_blocks))
+        return out
+
+    def counts(self):
+        w, r, f = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_sched_counts", lib().pa_sched_counts(self._h, ctypes.byref(w),
+                                                        ctypes.byref(r), ctypes.byref(f)))
+        return w.value, r.value, f.value

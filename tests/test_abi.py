@@ -9,14 +9,17 @@ import pytest
 from paged_kv_cache_19_amd import binding
 from tests.conftest import ROOT
 
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [os.path.join(ROOT, "include", "pa.h"), os.path.join(ROOT, "include", "pa_sched.h")]
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding.SIGNATURES)

@@ -1,0 +1,82 @@
+"""The native batch builder driving the hot path on the GPU: every step's
+slot mapping, block tables, sequence lengths and query offsets go straight
+into pa_reshape_and_cache and pa_chunked_prefill (with the builder's block
+reference counts as the cache hint), and each step's attention output is
+checked against the oracle on a CPU mirror of the pools.  Requests share
+prompt prefixes, so later requests read K/V written by earlier ones."""
+import math
+import random
+
+import pytest
+import torch
+
+import oracle.paged_attention as ref
+from paged_kv_cache_19_amd import binding
+from tests.gpu_common import bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def test_builder_drives_cache_write_and_chunked_prefill():
+    B, H, Hq, D, NB, V = 16, 8, 32, 128, 384, 97
+    g = torch.Generator().manual_seed(21)
+    ktab = torch.randn(V, H, D, generator=g).to(torch.bfloat16)
+    vtab = torch.randn(V, H, D, generator=g).to(torch.bfloat16)
+    qtab = torch.randn(V, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.full((NB, H, B, D), math.nan, dtype=torch.bfloat16)
+    vc = torch.full((NB, H, D, B), math.nan, dtype=torch.bfloat16)
+    kc_d, vc_d = kc.cuda(), vc.cuda()
+    nat = binding.BatchBuilder(NB, B, token_budget=256, chunk_tokens=96)
+    rng = random.Random(5)
+    prefix = [rng.randrange(V) for _ in range(40)]
+    tokens, gen, max_new = {}, {}, {}
+    for rid in range(8):
+        pre = prefix if rid % 2 == 0 else []
+        prompt = pre + [rng.randrange(V) for _ in range(rng.randrange(5, 260))]
+        tokens[rid], gen[rid], max_new[rid] = list(prompt), 0, rng.randrange(3, 12)
+        nat.add_request(rid, prompt, max_new_tokens=max_new[rid])
+    scale = D ** -0.5
+    worst = 0.0
+    for step in range(200):
+        b = nat.step()
+        S = len(b["req_ids"])
+        if S == 0:
+            if nat.counts()[:2] == (0, 0):
+                break
+            continue
+        qsl = b["query_start_loc"].tolist()
+        toks = []
+        for i, rid in enumerate(b["req_ids"].tolist()):
+            L, n = int(b["seq_lens"][i]), qsl[i + 1] - qsl[i]
+            toks += tokens[rid][L - n:L]
+        ti = torch.tensor(toks)
+        key, val, q = ktab[ti], vtab[ti], qtab[ti]
+        slots = torch.from_numpy(b["slot_mapping"])
+        bt = torch.from_numpy(b["block_tables"])
+        lens = torch.from_numpy(b["seq_lens"])
+        qsl_t = torch.from_numpy(b["query_start_loc"])
+        rc = torch.from_numpy(nat.block_refcounts())
+        binding.reshape_and_cache(key.cuda(), val.cuda(), kc_d, vc_d, slots.cuda())
+        out = binding.chunked_prefill(q.cuda(), kc_d, vc_d, bt.cuda(), lens.cuda(), qsl_t.cuda(),
+                                      int(lens.max()), max(qsl[i + 1] - qsl[i] for i in range(S)),
+                                      scale, block_refcounts=rc.cuda())
+        torch.cuda.synchronize()
+        kc, vc = ref.reshape_and_cache(kc, vc, key, val, slots)
+        expect = ref.paged_attention(q, kc, vc, bt, lens.tolist(), qsl, scale)
+        err = (out.cpu().double() - expect).abs().max().item()
+        worst = max(worst, err)
+        assert err <= 2e-2, (step, err)
+        # requests whose tokens are all computed take a sampled token, or end
+        # once they have generated max_new_tokens (as the builder does)
+        sampled = {}
+        for i, rid in enumerate(b["req_ids"].tolist()):
+            if int(b["seq_lens"][i]) == len(tokens[rid]) and gen[rid] < max_new[rid]:
+                sampled[rid] = (rid * 31 + len(tokens[rid]) * 7) % V
+        nat.update(sampled)
+        for rid, t in sampled.items():
+            tokens[rid].append(t)
+            gen[rid] += 1
+    log(f"[builder] {step + 1} steps, worst max abs err {worst:.3e}")
+    assert nat.counts() == (0, 0, 8)
+    assert torch.equal(bits(kc_d.cpu()), bits(kc)) and torch.equal(bits(vc_d.cpu()), bits(vc))
+
