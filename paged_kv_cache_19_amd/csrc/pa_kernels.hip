@@ -1092,6 +1092,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPrefillRows = 128;  // query rows per workgroup
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillStages = 4;  // LDS ring of K/V steps
+static_assert(kPrefillStages >= 3, "the pipelined loop reads two steps while one loads");
 
 // global_load_lds of 16 bytes: lane l's bytes land at lds_base + 16 * l.
 __device__ __forceinline__ void load_to_lds(const void* src, void* lds_base) {
@@ -1134,6 +1135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known uniform
   const int h = lane >> 5;
   const int c32 = lane & 31;
   const int S = a.num_seqs;
@@ -1220,10 +1222,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     int blk0 = k_begin >> lg;
     int wid = clampi(window(blk0), 0, a.num_blocks - 1);
     int wid_next = window(blk0 + 64);
-    auto block_id = [&](int pos) { return __shfl(wid, min(pos >> lg, v.nblk - 1) - blk0); };
     const int64_t blk_stride = (int64_t)a.num_kv_heads * B * D;
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * B * D;
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D * B;
+
+    // The blocks of one 32-key step are the same for the whole wave (32/B of
+    // them for B < 32, part of one block otherwise): the wave reads their
+    // ids from its id window with readlane, so every load address is a
+    // scalar block base plus a per-lane offset fixed for the whole item.
+    // A lane's K rows (tokens 8w..8w+7 of the step) lie in one block; its V
+    // chunk (8 tokens from 8*vc) in block vrel of the step.
+    const int nsb = B >= 32 ? 1 : 32 / B;
+    const int k_rel = (8 * wu) >> lg;  // wave-uniform
+    int k_off[IPW], v_off[IPW], v_rel[IPW];
+#pragma unroll
+    for (int x2 = 0; x2 < IPW; ++x2) {
+      const int x = w * IPW + x2;
+      const int t = x * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ ksw<D>(t);
+      k_off[x2] = (t & (B - 1)) * D + chunk * 8;
+      const int d = 16 * x + (lane >> 2);
+      const int vc = (lane & 3) ^ ((d >> 2) & 3);
+      v_rel[x2] = (8 * vc) >> lg;
+      v_off[x2] = d * B + ((8 * vc) & (B - 1));
+    }
 
     // This wave's share of one step: IPW 1 KiB pieces of the K tile and of
     // the V^T tile, written lane-contiguously into stage ``st``.
@@ -1233,18 +1255,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         wid = clampi(wid_next, 0, a.num_blocks - 1);
         wid_next = window(blk0 + 64);
       }
+      const int cb = (c >> lg) - blk0;
+      const int cmax = v.nblk - 1 - blk0;    // keys past the table reuse its last block
+      const int cin = B > 32 ? (c & (B - 1)) : 0;  // token offset of the step in its block
+      int sb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sb[j] = j < nsb ? __builtin_amdgcn_readlane(wid, min(cb + j, cmax)) : 0;
+      const int kid = k_rel == 0 ? sb[0] : (k_rel == 1 ? sb[1] : (k_rel == 2 ? sb[2] : sb[3]));
+      const uint16_t* kblk = kbase + (int64_t)kid * blk_stride + cin * D;
 #pragma unroll
       for (int x2 = 0; x2 < IPW; ++x2) {
         const int x = w * IPW + x2;
-        const int t = x * RPI + lane / CPR;
-        const int chunk = (lane % CPR) ^ ksw<D>(t);
-        const int pos = c + t;
-        load_to_lds(kbase + block_id(pos) * blk_stride + (pos & (B - 1)) * D + chunk * 8,
-                    &smem[st][0][x * 512]);
-        const int d = 16 * x + (lane >> 2);
-        const int vc = (lane & 3) ^ ((d >> 2) & 3);
-        const int vpos = c + 8 * vc;
-        load_to_lds(vbase + block_id(vpos) * blk_stride + (int64_t)d * B + (vpos & (B - 1)),
+        load_to_lds(kblk + k_off[x2], &smem[st][0][x * 512]);
+        const int vr = v_rel[x2];
+        const int vid = vr == 0 ? sb[0] : (vr == 1 ? sb[1] : (vr == 2 ? sb[2] : sb[3]));
+        load_to_lds(vbase + (int64_t)vid * blk_stride + v_off[x2] + cin,
                     &smem[st][1][x * 512]);
       }
     };
@@ -1256,15 +1282,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const float sl2 = a.scale_log2;  // > 0 (checked by the host)
     const int tk = sigma32(c32);
 
-    auto compute = [&](int st, int c) {
+    // S^T of one step (unscaled scores; the scale is applied in the exponent).
+    // All K fragments are read from LDS before the first MFMA so that their
+    // latency is paid once.
+    auto scores = [&](int st) {
       const uint16_t* kt = smem[st][0];
-      const uint16_t* vt = smem[st][1];
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8*>(kt + tk * D + (((2 * ks + h) ^ ksw<D>(tk)) * 8));
       f32x16 sacc = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(kt + tk * D + (((2 * ks + h) ^ ksw<D>(tk)) * 8));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
+      // schedule: the KS LDS reads, then the KS MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+      return sacc;
+    };
+
+    // Online softmax of one step's scores and the PV product.  The V^T
+    // fragments are read first: the exponentials hide their latency.
+    auto accumulate = [&](const f32x16& sacc, int st, int c) {
+      const uint16_t* vt = smem[st][1];
+      bf16x8 vf[2 * DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + c32;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          vf[2 * dt + k2] =
+              *reinterpret_cast<const bf16x8*>(vt + d * 32 + (((2 * k2 + h) ^ ((d >> 2) & 3)) * 8));
       }
       // Scores stay unscaled until the exponent: max(s * sl2) = max(s) * sl2.
       float sv[16];
@@ -1308,40 +1356,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
         l += __uint_as_float(q[0]) + __uint_as_float(q[1]);
       }
-      const bool tail = c + 32 > kv_wg;
+      if (c + 32 > kv_wg) {
+        // keys past the last visible one may be unwritten slots
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + c32;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vt + d * 32 + (((2 * k2 + h) ^ ((d >> 2) & 3)) * 8));
-          if (tail) {
-            // keys past the last visible one may be unwritten slots
+          for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (c + 16 * k2 + 8 * h + e >= kv_wg) vf[e] = static_cast<__bf16>(0.f);
-          }
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k2], o[dt], 0, 0, 0);
-        }
+              if (c + 16 * k2 + 8 * h + e >= kv_wg) vf[2 * dt + k2][e] = static_cast<__bf16>(0.f);
       }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt + k2], pf[k2], o[dt], 0, 0, 0);
     };
 
     // Ring of NS stages: step i lives in stage i % NS and is loaded NS-1
-    // iterations ahead.  Iteration i waits for this wave's loads of step i
-    // (the loads of the two younger steps may stay in flight); the barrier
-    // then publishes every wave's loads and also guarantees that all waves
-    // finished step i-1, whose stage the new loads overwrite.  The loads of
-    // steps past the end re-read the last step so that the count of loads
-    // in flight is the same in every iteration.
+    // steps ahead.  Software pipeline: iteration i issues the S^T MFMAs of
+    // step i+1 before the softmax and PV of step i, so the matrix unit runs
+    // while the vector unit computes the exponentials.  Iteration i therefore
+    // waits for this wave's loads of step i+1 (those of step i+2 may stay in
+    // flight); the barrier then publishes every wave's loads and guarantees
+    // that all waves finished step i-1, whose stage the new loads (step
+    // i+NS-1) overwrite.  Loads past the end re-read the last step so that
+    // the count of loads in flight is the same in every iteration.
     const int nsteps = (k_end - k_begin + 31) >> 5;
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p) dma(k_begin + 32 * min(p, nsteps - 1), p);
+    __builtin_amdgcn_s_waitcnt(0x3F70 | ((NS - 2) * DMA_PER_STEP));  // vmcnt: step 0 landed
+    __builtin_amdgcn_s_barrier();
+    f32x16 s_cur = wave_active ? scores(0) : f32x16{};
     for (int i = 0; i < nsteps; ++i) {
-      __builtin_amdgcn_s_waitcnt(0x3F70 | ((NS - 2) * DMA_PER_STEP));  // vmcnt
+      __builtin_amdgcn_s_waitcnt(0x3F70 | ((NS - 3) * DMA_PER_STEP));  // vmcnt: step i+1 landed
       __builtin_amdgcn_s_barrier();
       dma(k_begin + 32 * min(i + NS - 1, nsteps - 1), (i + NS - 1) % NS);
-      if (wave_active) compute(i % NS, k_begin + 32 * i);
+      if (wave_active) {
+        const f32x16 s_next = scores((i + 1) % NS);  // step i+1 (past the end: unused)
+        accumulate(s_cur, i % NS, k_begin + 32 * i);
+        s_cur = s_next;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): the ring is quiet
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
