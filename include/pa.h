@@ -160,9 +160,15 @@ int pa_decode(void* out, const void* query, const void* k_cache,
 
 /*
  * Workspace for pa_chunked_prefill: fp32 partials for the query-chunk rows
- * (num_tokens * num_q_heads rows, one slot per kv_split_tokens keys, 2048
- * when 0), fp32 pieces for the balanced decode of single-token rows
- * (num_seqs * num_q_heads rows) and a small header.  Returns 0 for invalid
+ * (num_tokens * num_q_heads rows) and an int32 piece count per such row,
+ * fp32 pieces for the balanced decode of single-token rows
+ * (num_seqs * num_q_heads rows) and a small header.
+ * kv_split_tokens: 0 lets the library spread the chunk rows' keys evenly
+ * over the GPU (each workgroup takes an equal run of 32-key steps of all
+ * row tiles, so a tile may be cut into a few pieces); a positive multiple
+ * of 64 fixes that run to kv_split_tokens keys instead (and, for fp32 or
+ * small-block caches, the split size of the vector-ALU path, 2048 keys when
+ * 0).  Pass the same value to pa_chunked_prefill.  Returns 0 for invalid
  * arguments.
  */
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,

@@ -15,7 +15,12 @@
 namespace {
 
 constexpr int kDefaultSplitTokens = 512;        // decode rows on the fixed-split path
-constexpr int kDefaultChunkSplitTokens = 2048;  // query-chunk rows
+constexpr int kDefaultChunkSplitTokens = 2048;  // query-chunk rows on the vector-ALU path
+// Chunk kernel (MFMA path): a workgroup range is at least this many 32-key
+// steps, and long enough that no row tile is cut into more than
+// kChunkPieces pieces.
+constexpr int kMinChunkSteps = 16;
+constexpr int kChunkPieces = 4;
 // The balanced decode keeps every sequence's step prefix sum in LDS.
 constexpr int kMaxBalancedSeqs = 4096;
 constexpr size_t kAlign = 256;
@@ -52,14 +57,18 @@ struct WorkspacePlan {
   int split_tokens = 0;   // fixed-split / chunk path: keys per split
   int max_splits = 0;     // fixed-split / chunk path: partial slots per row
   int max_pieces = 0;     // balanced decode: partial slots per row (0: unused)
+  int chunk_steps = 0;    // chunk kernel: steps per workgroup range (minimum when auto)
+  int chunk_auto = 0;
   size_t a_o = 0, a_ml = 0;  // region A: [T*Hq, max_splits] partials (o, then (m, l))
+  size_t rp = 0;             // chunk rows: [T*Hq] piece counts
   size_t b_o = 0, b_ml = 0;  // region B: [S*Hq, max_pieces] balanced-decode pieces
   size_t header = 0;         // balanced-decode header
   size_t total = 0;
 };
 
 // Workspace layout: region A (fixed-split and query-chunk partials, one row
-// per query token and head) | region B (balanced-decode pieces, one row per
+// per query token and head; then, for pa_chunked_prefill, the piece count of
+// each row) | region B (balanced-decode pieces, one row per
 // sequence and head) | header (step total, wave count, per-sequence step
 // prefix sums).  pa_decode's two paths share one region (rows = sequences),
 // so its size is the larger of the two slot counts.
@@ -76,7 +85,16 @@ bool plan_workspace(int num_tokens, int num_seqs, int num_q_heads, int head_dim,
   p->max_pieces = (steps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
   const size_t ob = (size_t)head_dim * sizeof(float), mlb = 2 * sizeof(float);
   if (chunk_entry) {
+    // The chunk kernel cuts each row tile's steps into at most
+    // ceil(steps / chunk_steps) + 1 pieces; the vector-ALU path into
+    // max_splits fixed splits.  Region A holds the larger count.
+    p->chunk_auto = kv_split_tokens == 0;
+    p->chunk_steps = p->chunk_auto
+                         ? std::max(kMinChunkSteps, (steps + kChunkPieces - 2) / (kChunkPieces - 1))
+                         : st / 32;
+    p->max_splits = std::max(p->max_splits, (steps + p->chunk_steps - 1) / p->chunk_steps + 1);
     const size_t ra = (size_t)num_tokens * num_q_heads * p->max_splits;
+    p->rp = align_up((size_t)num_tokens * num_q_heads * sizeof(int32_t));
     const size_t rb = (size_t)num_seqs * num_q_heads * p->max_pieces;
     p->a_o = align_up(ra * ob);
     p->a_ml = align_up(ra * mlb);
@@ -90,7 +108,7 @@ bool plan_workspace(int num_tokens, int num_seqs, int num_q_heads, int head_dim,
     p->a_ml = align_up(r * mlb);
   }
   p->header = align_up(16 + (size_t)(num_seqs + 1) * 4);
-  p->total = p->a_o + p->a_ml + p->b_o + p->b_ml + p->header;
+  p->total = p->a_o + p->a_ml + p->rp + p->b_o + p->b_ml + p->header;
   return true;
 }
 
@@ -263,6 +281,12 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   a.kv_fp8 = f8.kv_fp8;
   a.k_scales = f8.k_scales;
   a.v_scales = f8.v_scales;
+  // Piece counts per row: written by the MFMA chunk kernel only (the
+  // vector-ALU path's merge derives its split count from split_tokens).
+  a.row_pieces = plan.rp && mfma ? reinterpret_cast<int32_t*>(ws + plan.a_o + plan.a_ml) : nullptr;
+  a.chunk_steps = plan.chunk_steps;
+  a.chunk_auto = plan.chunk_auto;
+  ws += plan.rp;  // region B and the header follow the piece counts
   void* header = ws + plan.a_o + plan.a_ml + plan.b_o + plan.b_ml;
   hipError_t err;
   if (chunk_entry) {

@@ -27,6 +27,9 @@ struct AttnArgs {
   int32_t block_size, log2_block, num_blocks;
   int32_t split_tokens, max_splits, max_query_len;
   int32_t sk_slots;         // pieces per row in sk_part_*
+  int32_t* row_pieces;      // [T * Hq] chunk rows: pieces of part_o the row's keys were cut into
+  int32_t chunk_steps;      // chunk kernel: 32-key steps per workgroup range (minimum when auto)
+  int32_t chunk_auto;       // 1: ranges sized to spread all steps over the resident workgroups
   float scale_log2;         // scale * log2(e)
   int32_t bf16;             // 1: bf16 elements, 0: fp32 (q, out and, unless kv_fp8, the cache)
   int32_t kv_fp8;           // 1: e4m3 cache with per-(block, KV head) scales, bf16 q/out

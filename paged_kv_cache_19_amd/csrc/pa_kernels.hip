@@ -1065,10 +1065,23 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
 
 // ---------------------------------------------------------------------------
 // Query-chunk attention (chunked prefill) on v_mfma_f32_32x32x16_bf16 with
-// K/V staged in LDS.  One workgroup of 4 waves serves 128 query rows
-// (row = j * G + g) of one (sequence, KV head) and one split of keys; each
-// wave owns 32 rows, so one 32-key step costs every wave 2*D/16 MFMAs against
-// 16*D bytes of K/V that the whole workgroup loads once.
+// K/V staged in LDS.
+//
+// Work.  A unit is (sequence with q_len > 1, KV head, tile of 256 query rows,
+// row = j * G + g for chunk token j and group head g).  It needs
+// ceil(klim / 32) steps of 32 keys, klim being the causal key limit of its
+// last row.  The steps of all units, laid end to end (sequence, KV head,
+// tile; tile fastest, so that the tiles sharing one stretch of K/V are
+// neighbours), are cut into ranges of equal length, one range per resident
+// workgroup ("stream-K").  A unit that a range boundary cuts leaves one
+// partial (o, m, l) per piece; merge_kernel combines them.  Ranges go to
+// workgroups so that each XCD (workgroups are dealt to the 8 XCDs
+// round-robin) takes a contiguous run, which keeps a unit's K/V in one L2.
+//
+// One workgroup of 4 waves per CU (one wave per SIMD, up to 512 registers).
+// A wave owns 64 query rows as two halves of 32, so every K and V fragment
+// it reads from LDS feeds two MFMAs.  Per 32-key step a wave issues 16
+// MFMAs for S^T = K Q^T and 16 for O^T = V^T P^T.
 //
 // S^T = K Q^T (A = K rows of the step, B = Q^T): the accumulator gives lane
 // l the 16 scores of query row l%32 at MFMA rows (r/4)*8 + 4*(l/32) + r%4.
@@ -1078,21 +1091,35 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
 // k-th 16-key MFMA step.  In O^T every register of lane l belongs to query
 // row l%32, so the online-softmax rescale is lane-local.
 //
-// LDS holds two stages of [K tile 32 x D | V^T tile D x 32].  Tiles are
-// written 16 bytes per lane contiguously and read in MFMA operand order;
-// the 16-byte chunks are XOR-swizzled so that both the K reads (32 token
-// rows, one chunk each) and the V^T reads (32 head_dim rows) are free of
-// bank conflicts.  The tiles are filled by direct global->LDS loads
-// (16 bytes per lane, no registers) kPrefillStages-1 steps ahead of the
-// step being computed; each wave waits for its own loads with vmcnt and a
-// workgroup barrier publishes the stage.
+// LDS holds a ring of kPrefillStages steps of [K tile 32 x D | V^T tile],
+// filled by direct global->LDS loads (16 bytes per lane, no registers)
+// kPrefillStages-1 steps ahead of the step being computed.  Every load
+// instruction reads from one physical block, so its address is a scalar
+// block base plus a per-lane offset fixed for the whole kernel.  K rows keep
+// the pool's token-row order; the V^T tile is block-major ([block of the
+// step][head_dim row][8-key chunk]) so that it, too, copies whole runs of one
+// block.  The 16-byte chunks are XOR-swizzled so that the MFMA operand reads
+// (ds_read_b128, 16 lanes per LDS cycle) touch 16 distinct bank groups.
+// Each wave waits for its own loads with vmcnt; one workgroup barrier per
+// step publishes the stage and frees the oldest one.
 // ---------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPrefillRows = 128;  // query rows per workgroup
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillStages = 4;  // LDS ring of K/V steps
-static_assert(kPrefillStages >= 3, "the pipelined loop reads two steps while one loads");
+// Shape of the chunk kernel per head_dim: query rows per wave (32 * halves)
+// and waves per workgroup; a unit is the workgroup's rows.
+template <int D>
+struct PrefillShape {
+  static constexpr int kHalves = 1;
+  static constexpr int kWaves = D == 128 ? 8 : 4;
+  static constexpr int kRows = 32 * kHalves * kWaves;
+};
+constexpr int kPrefillGroup = 4;                        // steps between barriers
+constexpr int kPrefillStages = 2 * kPrefillGroup + 1;   // LDS ring of K/V steps
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their "no wait" maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // global_load_lds of 16 bytes: lane l's bytes land at lds_base + 16 * l.
 __device__ __forceinline__ void load_to_lds(const void* src, void* lds_base) {
@@ -1113,318 +1140,441 @@ __device__ __forceinline__ int ksw(int t) {
   return (t / (128 / D)) % (D / 8);
 }
 
-// Work items of the chunk kernel: (sequence with q_len > 1, split, KV head,
-// row tile), row tile fastest so that the 128-row tiles sharing one
-// (sequence, KV head, split) -- and so one stretch of K/V -- are consecutive.
-// The kernel is persistent: a fixed set of resident workgroups walks the
-// item list in rounds; within a round the workgroups of one XCD take a
-// contiguous run of items (workgroups are dealt to the 8 XCDs round-robin),
-// so tiles that share K/V run together on one XCD and share its L2.
+// Steps of 32 keys that tile `tile` of a sequence needs: up to the causal
+// limit of its last row, capped by what the table addresses.
+__device__ __forceinline__ int tile_steps(int rows, int tile, int nrows, int G, int L, int qn,
+                                          int kcap) {
+  const int row_last = min((tile + 1) * rows, nrows) - 1;
+  const int klim = min(L - qn + row_last / G + 1, kcap);
+  return klim > 0 ? (klim + 31) >> 5 : 0;
+}
+
+// Steps of all units of sequence s for one KV head (0 for decode rows).
+__device__ __forceinline__ int seq_unit_steps(const AttnArgs& a, int s, int G, int rows) {
+  int r0, qn;
+  seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+  if (qn <= 1) return 0;
+  const int L = a.seq_lens[s];
+  const int kcap = table_blocks(L, a.log2_block, a.max_blocks) << a.log2_block;
+  const int nrows = qn * G;
+  const int tiles = (nrows + rows - 1) / rows;
+  int n = 0;
+  for (int t = 0; t < tiles; ++t) n += tile_steps(rows, t, nrows, G, L, qn, kcap);
+  return n;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
-    AttnArgs a, int num_wgs) {
-  constexpr int KS = D / 16;                       // S^T MFMA steps over head_dim
-  constexpr int DT = D / 32;                       // O^T head_dim tiles
-  constexpr int CPR = D / 8;                       // 16-byte chunks per K row
-  constexpr int RPI = 1024 / (2 * D);              // K rows per 1 KiB load
-  constexpr int IPW = (D / 16) / kPrefillWaves;    // 1 KiB loads per wave per tile
+__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
+    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
+void prefill_kernel(AttnArgs a, int num_wgs) {
+  constexpr int H = PrefillShape<D>::kHalves;    // 32-row halves per wave
+  constexpr int NW = PrefillShape<D>::kWaves;
+  constexpr int ROWS = PrefillShape<D>::kRows;
+  constexpr int KS = D / 16;                     // S^T MFMA steps over head_dim
+  constexpr int DT = D / 32;                     // O^T head_dim tiles
+  constexpr int CPR = D / 8;                     // 16-byte chunks per K row
+  constexpr int RPI = 1024 / (2 * D);            // K rows per 1 KiB load
+  constexpr int IPW = (D / 16) / NW;            // 1 KiB loads per wave per tile
+  static_assert(IPW >= 1, "every wave loads part of each tile");
   constexpr int NS = kPrefillStages;
-  constexpr int DMA_PER_STEP = 2 * IPW;            // loads per wave per step
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NS][2][32 * D];
-  extern __shared__ int item_prefix[];             // [num_seqs + 1]
+  constexpr int GS = kPrefillGroup;
+  constexpr int TILE = 32 * D;                   // elements of one K or V^T tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NS][2][TILE];
+  extern __shared__ int seq_prefix[];            // [num_seqs + 1] steps
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // known wave-uniform
   const int h = lane >> 5;
   const int c32 = lane & 31;
   const int S = a.num_seqs;
   const int G = a.num_q_heads / a.num_kv_heads;
+  const int Hkv = a.num_kv_heads;
   const int lg = a.log2_block;
   const int B = 1 << lg;
-  const int ST = a.split_tokens;
+  const int Bs = min(B, 32);     // keys of one block inside a step
+  const int cpb = Bs >> 3;       // 8-key chunks of one block inside a step (1, 2, 4)
+  const int lcpb = cpb == 4 ? 2 : cpb - 1;
 
-  // Items per sequence, then their prefix sums (one thread per sequence,
-  // a simple serial scan over 256-sequence segments).
-  for (int s = tid; s < S; s += 256) {
-    int r0, qn;
-    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-    int n = 0;
-    if (qn > 1) {
-      const int L = a.seq_lens[s];
-      const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
-      const int tiles = (qn * G + kPrefillRows - 1) / kPrefillRows;
-      const int splits = min((kl + ST - 1) / ST, a.max_splits);
-      n = kl > 0 ? tiles * a.num_kv_heads * splits : 0;
-    }
-    item_prefix[s + 1] = n;
-  }
+  // Steps per sequence (all KV heads), then their prefix sums.
+  for (int s = tid; s < S; s += 64 * NW) seq_prefix[s + 1] = Hkv * seq_unit_steps(a, s, G, ROWS);
   __syncthreads();
   if (tid == 0) {
-    item_prefix[0] = 0;
-    for (int s = 0; s < S; ++s) item_prefix[s + 1] += item_prefix[s];
+    seq_prefix[0] = 0;
+    for (int s = 0; s < S; ++s) seq_prefix[s + 1] += seq_prefix[s];
   }
   __syncthreads();
-  const int total = item_prefix[S];
+  const int N = seq_prefix[S];
+  if (N == 0) return;
+  const int chunk = a.chunk_auto ? max((N + num_wgs - 1) / num_wgs, a.chunk_steps) : a.chunk_steps;
+  const int nranges = (N + chunk - 1) / chunk;
   const int wg = blockIdx.x;
 
-  for (int k = (wg & 7) * (num_wgs >> 3) + (wg >> 3); k < total; k += num_wgs) {
-    // -- decode item k -------------------------------------------------------
+  // Per-lane pieces of the load and read addresses, fixed for the kernel.
+  int k_voff[IPW], v_voff[IPW], v_bi[IPW];
+#pragma unroll
+  for (int x2 = 0; x2 < IPW; ++x2) {
+    const int x = w * IPW + x2;
+    const int t = x * RPI + lane / CPR;  // token row of the step
+    const int chunk16 = (lane % CPR) ^ ksw<D>(t);
+    k_voff[x2] = ((lane / CPR) * D + chunk16 * 8) * 2;
+    const int p = 64 * x + lane;              // 16-byte position in the V^T tile
+    v_bi[x2] = p / (D * cpb);                 // block of the step
+    const int d = (p % (D * cpb)) >> lcpb;    // head_dim row
+    const int vs = (d >> (4 - lcpb)) & (cpb - 1);
+    const int u = (p & (cpb - 1)) ^ vs;       // 8-key chunk inside the block
+    v_voff[x2] = (d * B + 8 * u) * 2;
+  }
+  const int tk = sigma32(c32);
+  int k_roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_roff[ks] = tk * D + (((2 * ks + h) ^ ksw<D>(tk)) * 8);
+  int v_roff[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int c = 2 * k2 + h;  // 8-key chunk of the step
+    const int bi = c >> lcpb, u = c & (cpb - 1);
+    const int vs = (c32 >> (4 - lcpb)) & (cpb - 1);
+    v_roff[k2] = (bi * D * cpb + c32 * cpb + (u ^ vs)) * 8;
+  }
+  const float sl2 = a.scale_log2;  // > 0 (checked by the host)
+  const int64_t blk_stride = (int64_t)Hkv * B * D;
+
+  for (int r = (wg & 7) * (num_wgs >> 3) + (wg >> 3); r < nranges; r += num_wgs) {
+    int g = r * chunk;
+    const int gend = min(g + chunk, N);
+    // -- unit holding step g ---------------------------------------------
     int s;
     {
       int lo = 0, hi = S - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (item_prefix[mid] <= k) lo = mid;
+        if (seq_prefix[mid] <= g) lo = mid;
         else hi = mid - 1;
       }
       s = lo;
     }
-    int r0, qn;
-    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-    const int nrows = qn * G;
-    const int tiles = (nrows + kPrefillRows - 1) / kPrefillRows;
-    int rem = k - item_prefix[s];
-    const int tile = rem % tiles;
-    rem /= tiles;
-    const int kvh = rem % a.num_kv_heads;
-    const int split = rem / a.num_kv_heads;
-    const int L = a.seq_lens[s];
-    const SeqView v = seq_view(a, s, kvh, L, r0, qn);
-    const int row0 = tile * kPrefillRows;
-    const int row_last = min(row0 + kPrefillRows, nrows) - 1;
-    const int kv_wg = min(L - qn + row_last / G + 1, v.kcap);
-    const int k_begin = split * ST;
-    if (k_begin >= kv_wg) continue;  // workgroup-uniform
-    const int k_end = min(k_begin + ST, kv_wg);
-
-    const int wrow0 = row0 + 32 * w;
-    const bool wave_active = wrow0 < nrows;
-    const int kv_wmin = wave_active ? min(L - qn + wrow0 / G + 1, v.kcap) : 0;
-    const int row = wrow0 + c32;
-    const bool row_ok = row < nrows;
-    const int jrow = row_ok ? row / G : 0;
-    const int grow = row_ok ? row - jrow * G : 0;
-    const int klim = row_ok ? min(L - qn + jrow + 1, v.kcap) : 0;
-
-    bf16x8 qf[KS];
+    int rem = g - seq_prefix[s];
+    int kvh = 0, tile = 0;
     {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                           ((int64_t)(r0 + jrow) * a.num_q_heads + kvh * G + grow) * D + 8 * h;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? load_bf16x8(qp + 16 * ks) : bf16x8{};
+      const int per_head = (seq_prefix[s + 1] - seq_prefix[s]) / Hkv;
+      kvh = rem / per_head;
+      rem -= kvh * per_head;
     }
-
-    const int64_t trow = (int64_t)s * a.max_blocks;
-    // Block ids are clamped into the pool when a window becomes current, not
-    // when it is loaded: the prefetched next window is not waited for early.
-    auto window = [&](int b0) { return a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)]; };
-    int blk0 = k_begin >> lg;
-    int wid = clampi(window(blk0), 0, a.num_blocks - 1);
-    int wid_next = window(blk0 + 64);
-    const int64_t blk_stride = (int64_t)a.num_kv_heads * B * D;
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * B * D;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D * B;
-
-    // The blocks of one 32-key step are the same for the whole wave (32/B of
-    // them for B < 32, part of one block otherwise): the wave reads their
-    // ids from its id window with readlane, so every load address is a
-    // scalar block base plus a per-lane offset fixed for the whole item.
-    // A lane's K rows (tokens 8w..8w+7 of the step) lie in one block; its V
-    // chunk (8 tokens from 8*vc) in block vrel of the step.
-    const int nsb = B >= 32 ? 1 : 32 / B;
-    const int k_rel = (8 * wu) >> lg;  // wave-uniform
-    int k_off[IPW], v_off[IPW], v_rel[IPW];
-#pragma unroll
-    for (int x2 = 0; x2 < IPW; ++x2) {
-      const int x = w * IPW + x2;
-      const int t = x * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ ksw<D>(t);
-      k_off[x2] = (t & (B - 1)) * D + chunk * 8;
-      const int d = 16 * x + (lane >> 2);
-      const int vc = (lane & 3) ^ ((d >> 2) & 3);
-      v_rel[x2] = (8 * vc) >> lg;
-      v_off[x2] = d * B + ((8 * vc) & (B - 1));
-    }
-
-    // This wave's share of one step: IPW 1 KiB pieces of the K tile and of
-    // the V^T tile, written lane-contiguously into stage ``st``.
-    auto dma = [&](int c, int st) {
-      if ((c >> lg) - blk0 >= 64) {  // wave-uniform: next window of block ids
-        blk0 += 64;
-        wid = clampi(wid_next, 0, a.num_blocks - 1);
-        wid_next = window(blk0 + 64);
-      }
-      const int cb = (c >> lg) - blk0;
-      const int cmax = v.nblk - 1 - blk0;    // keys past the table reuse its last block
-      const int cin = B > 32 ? (c & (B - 1)) : 0;  // token offset of the step in its block
-      int sb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sb[j] = j < nsb ? __builtin_amdgcn_readlane(wid, min(cb + j, cmax)) : 0;
-      const int kid = k_rel == 0 ? sb[0] : (k_rel == 1 ? sb[1] : (k_rel == 2 ? sb[2] : sb[3]));
-      const uint16_t* kblk = kbase + (int64_t)kid * blk_stride + cin * D;
-#pragma unroll
-      for (int x2 = 0; x2 < IPW; ++x2) {
-        const int x = w * IPW + x2;
-        load_to_lds(kblk + k_off[x2], &smem[st][0][x * 512]);
-        const int vr = v_rel[x2];
-        const int vid = vr == 0 ? sb[0] : (vr == 1 ? sb[1] : (vr == 2 ? sb[2] : sb[3]));
-        load_to_lds(vbase + (int64_t)vid * blk_stride + v_off[x2] + cin,
-                    &smem[st][1][x * 512]);
-      }
+    bool located = false;
+    // Next unit in (sequence, KV head, tile) order; false past the last one.
+    auto advance = [&](int tiles) {
+      if (++tile < tiles) return true;
+      tile = 0;
+      if (++kvh < Hkv) return true;
+      kvh = 0;
+      do {
+        ++s;
+      } while (s < S && seq_prefix[s + 1] == seq_prefix[s]);
+      return s < S;
     };
-
-    float m = neg_inf(), l = 0.f;
-    f32x16 o[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-    const float sl2 = a.scale_log2;  // > 0 (checked by the host)
-    const int tk = sigma32(c32);
-
-    // S^T of one step (unscaled scores; the scale is applied in the exponent).
-    // All K fragments are read from LDS before the first MFMA so that their
-    // latency is paid once.
-    auto scores = [&](int st) {
-      const uint16_t* kt = smem[st][0];
-      bf16x8 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = *reinterpret_cast<const bf16x8*>(kt + tk * D + (((2 * ks + h) ^ ksw<D>(tk)) * 8));
-      f32x16 sacc = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc, 0, 0, 0);
-      // schedule: the KS LDS reads, then the KS MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
-      return sacc;
-    };
-
-    // Online softmax of one step's scores and the PV product.  The V^T
-    // fragments are read first: the exponentials hide their latency.
-    auto accumulate = [&](const f32x16& sacc, int st, int c) {
-      const uint16_t* vt = smem[st][1];
-      bf16x8 vf[2 * DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + c32;
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          vf[2 * dt + k2] =
-              *reinterpret_cast<const bf16x8*>(vt + d * 32 + (((2 * k2 + h) ^ ((d >> 2) & 3)) * 8));
+    while (g < gend) {
+      int r0, qn;
+      seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+      const int L = a.seq_lens[s];
+      const SeqView v = seq_view(a, s, kvh, L, r0, qn);
+      const int nrows = qn * G;
+      const int tiles = (nrows + ROWS - 1) / ROWS;
+      if (!located) {  // tile holding step rem of this (sequence, KV head)
+        for (;;) {
+          const int n = tile_steps(ROWS, tile, nrows, G, L, qn, v.kcap);
+          if (rem < n) break;
+          rem -= n;
+          ++tile;
+        }
+        located = true;
       }
-      // Scores stay unscaled until the exponent: max(s * sl2) = max(s) * sl2.
-      float sv[16];
+      const int nst = tile_steps(ROWS, tile, nrows, G, L, qn, v.kcap);
+      if (nst == 0) {  // rows that see no keys (q_len > seq_len): nothing to do
+        if (!advance(tiles)) break;
+        continue;
+      }
+      const int a_step = rem;
+      const int b_step = min(nst, rem + (gend - g));
+      const int u_first = (g - a_step) / chunk;            // range of the unit's first step
+      const int u_last = (g - a_step + nst - 1) / chunk;   // range of its last step
+      const int npieces = u_last - u_first + 1;
+      const int slot = r - u_first;
+
+      // -- one piece: steps [a_step, b_step) of unit (s, kvh, tile) --------
+      const int row0 = tile * ROWS;
+      const int row_last = min(row0 + ROWS, nrows) - 1;
+      const int kv_t = min(L - qn + row_last / G + 1, v.kcap);  // keys the unit sees
+      const int k_begin = 32 * a_step;
+      const int nsteps = b_step - a_step;
+      const int wrow0 = row0 + 32 * H * w;
+      const bool wave_active = wrow0 < nrows;
+      const int kv_wmin = wave_active ? min(L - qn + wrow0 / G + 1, v.kcap) : 0;
+
+      int jr[H], gr[H], klim[H];
+      bool ok[H];
+      bf16x8 qf[H][KS];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
-      if (c + 32 > kv_wmin) {
+      for (int hf = 0; hf < H; ++hf) {
+        const int row = wrow0 + 32 * hf + c32;
+        ok[hf] = row < nrows;
+        jr[hf] = ok[hf] ? row / G : 0;
+        gr[hf] = ok[hf] ? row - jr[hf] * G : 0;
+        klim[hf] = ok[hf] ? min(L - qn + jr[hf] + 1, v.kcap) : 0;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(r0 + jr[hf]) * a.num_q_heads + kvh * G + gr[hf]) * D + 8 * h;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = sigma32((r >> 2) * 8 + 4 * h + (r & 3));
-          sv[r] = (c + tok < klim) ? sv[r] : neg_inf();
+        for (int ks = 0; ks < KS; ++ks) qf[hf][ks] = ok[hf] ? load_bf16x8(qp + 16 * ks) : bf16x8{};
+      }
+
+      const int64_t trow = (int64_t)s * a.max_blocks;
+      // Block ids: a window of 64 logical blocks, one per lane, read with
+      // readlane.  Ids are clamped when a window becomes current, not when it
+      // is loaded: the prefetched next window is not waited for early.
+      auto window = [&](int b0) { return a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)]; };
+      int blk0 = k_begin >> lg;
+      int wid = clampi(window(blk0), 0, a.num_blocks - 1);
+      int wid_next = window(blk0 + 64);
+      const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * B * D;
+      const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D * B;
+
+      // This wave's share of one step (key c) into stage st: IPW 1 KiB pieces
+      // of the K tile and of the V^T tile, each from one block.
+      auto dma = [&](int c, int st) {
+        if ((c >> lg) - blk0 >= 64) {  // wave-uniform: next window of block ids
+          blk0 += 64;
+          wid = clampi(wid_next, 0, a.num_blocks - 1);
+          wid_next = window(blk0 + 64);
+        }
+        const int cb = (c >> lg) - blk0;
+        const int cmax = v.nblk - 1 - blk0;          // keys past the table reuse its last block
+        const int cin = B > 32 ? (c & (B - 1)) : 0;  // token offset of the step in its block
+#pragma unroll
+        for (int x2 = 0; x2 < IPW; ++x2) {
+          const int x = w * IPW + x2;
+          const int kb = (x * RPI) >> lg;  // block of these K rows inside the step
+          const int kid = __builtin_amdgcn_readlane(wid, min(cb + kb, cmax));
+          const char* ksrc = reinterpret_cast<const char*>(
+              kbase + (int64_t)kid * blk_stride + (cin + ((x * RPI) & (Bs - 1))) * D);
+          load_to_lds(ksrc + k_voff[x2], &smem[st][0][x * 512]);
+          const int vb = __builtin_amdgcn_readfirstlane(v_bi[x2]);
+          const int vid = __builtin_amdgcn_readlane(wid, min(cb + vb, cmax));
+          const char* vsrc =
+              reinterpret_cast<const char*>(vbase + (int64_t)vid * blk_stride + cin);
+          load_to_lds(vsrc + v_voff[x2], &smem[st][1][x * 512]);
+        }
+      };
+
+      float m[H], l[H];
+      f32x16 o[H][DT];
+#pragma unroll
+      for (int hf = 0; hf < H; ++hf) {
+        m[hf] = neg_inf();
+        l[hf] = 0.f;
+      }
+#pragma unroll
+      for (int hf = 0; hf < H; ++hf)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[hf][dt] = f32x16{};
+
+      // S^T of one step for every half (unscaled scores).
+      auto scores = [&](int st, f32x16* sc) {
+        const uint16_t* kt = smem[st][0];
+        bf16x8 kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kt + k_roff[ks]);
+#pragma unroll
+        for (int hf = 0; hf < H; ++hf) sc[hf] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf)
+            sc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[hf][ks], sc[hf], 0, 0, 0);
+      };
+
+      // Keys past a row's limit get score -inf (scores sc of the step at key c).
+      auto mask_scores = [&](f32x16* sc, int c) {
+#pragma unroll
+        for (int hf = 0; hf < H; ++hf)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tok = 16 * (r >> 3) + 8 * h + (r & 7);
+            sc[hf][r] = c + tok < klim[hf] ? sc[hf][r] : neg_inf();
+          }
+      };
+      // Row maxima of (masked) scores, in log2 units.
+      auto row_max = [&](const f32x16* sc, float* mx) {
+#pragma unroll
+        for (int hf = 0; hf < H; ++hf) {
+          float t = sc[hf][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) t = fmaxf(t, sc[hf][r]);
+          auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+          mx[hf] = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])) * sl2;
+        }
+      };
+
+      // Ring of NS = 2 * GS + 1 stages, filled GS steps at a time.  Before
+      // group g (steps g*GS .. g*GS + GS - 1) every wave waits for its own
+      // loads of steps up to g*GS + GS (the group and the step after it,
+      // whose K the group's last step reads), and one barrier publishes
+      // everyone's loads and guarantees that all waves left group g-1; the
+      // loads of steps g*GS + GS + 1 .. g*GS + 2*GS then go to the stages
+      // group g-1 used.  Between barriers the waves of a workgroup run
+      // freely, so the two waves sharing a SIMD drift apart and overlap
+      // their matrix and vector work.  Loads past the end re-read the last
+      // step.
+      //
+      // Within a step, the S^T of step i+1 is computed between the (masked)
+      // scores of step i and its softmax and PV; the maxima of step i+1 are
+      // taken at the end of step i, while its PV MFMAs run, and the (rare)
+      // rescale of the accumulators happens at the top of step i+1.
+      int st_load = 0;  // stage of the next load
+      auto load_step = [&](int p) {
+        dma(k_begin + 32 * min(p, nsteps - 1), st_load);
+        st_load = st_load + 1 == NS ? 0 : st_load + 1;
+      };
+#pragma unroll
+      for (int p = 0; p <= GS; ++p) load_step(p);
+      f32x16 cur[H];
+      float mxn[H];
+      bool grow = false;  // some row's maximum rose by more than kLazyRescaleLog2
+      int st_cur = 0;     // stage of step i
+      for (int g0 = 0; g0 < nsteps; g0 += GS) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int p = GS + 1; p <= 2 * GS; ++p) load_step(g0 + p);
+        if (!wave_active) continue;
+        if (g0 == 0) {
+          scores(0, cur);
+          if (k_begin + 32 > kv_wmin) mask_scores(cur, k_begin);
+          row_max(cur, mxn);
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf) m[hf] = mxn[hf];
+        }
+        const int i_end = min(g0 + GS, nsteps);
+        for (int i = g0; i < i_end; ++i) {
+          const int st_next = st_cur + 1 == NS ? 0 : st_cur + 1;
+          const int c = k_begin + 32 * i;
+          if (grow) {
+            rare_branch();
+#pragma unroll
+            for (int hf = 0; hf < H; ++hf) {
+              const float mnew = fmaxf(m[hf], mxn[hf]);
+              const float alpha = fast_exp2(m[hf] - ((mnew == neg_inf()) ? 0.f : mnew));
+              l[hf] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[hf][dt][r] *= alpha;
+              m[hf] = mnew;
+            }
+          }
+          f32x16 nxt[H];
+          scores(st_next, nxt);
+          bf16x8 pf[H][2];
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf) {
+            const float nm = (m[hf] == neg_inf()) ? 0.f : -m[hf];
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float p = fast_exp2(fmaf(cur[hf][r], sl2, nm));
+              ps += p;
+              pf[hf][r >> 3][r & 7] = static_cast<__bf16>(p);
+            }
+            auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+            l[hf] += __uint_as_float(q[0]) + __uint_as_float(q[1]);
+          }
+          const uint16_t* vt = smem[st_cur][1];
+          bf16x8 vf[DT][2];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+              vf[dt][k2] = *reinterpret_cast<const bf16x8*>(vt + v_roff[k2] + dt * 32 * cpb * 8);
+          if (c + 32 > kv_t) {
+            // keys past the unit's last visible one may be unwritten slots:
+            // their V must not reach the accumulators even with p = 0
+            rare_branch();
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+              const int lim = kv_t - (c + 16 * k2 + 8 * h);  // valid keys of this lane's 8
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) {
+                u32x4 bits = __builtin_bit_cast(u32x4, vf[dt][k2]);
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                  const uint32_t keep = (2 * e2 < lim ? 0xFFFFu : 0u) | (2 * e2 + 1 < lim ? 0xFFFF0000u : 0u);
+                  bits[e2] &= keep;
+                }
+                vf[dt][k2] = __builtin_bit_cast(bf16x8, bits);
+              }
+            }
+          }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+              for (int hf = 0; hf < H; ++hf)
+                o[hf][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][k2], pf[hf][k2], o[hf][dt], 0, 0, 0);
+          // next step's scores: mask, maxima, rescale decision
+          if (c + 64 > kv_wmin) mask_scores(nxt, c + 32);
+          row_max(nxt, mxn);
+          bool g = false;
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf) g = g || mxn[hf] > m[hf] + kLazyRescaleLog2;
+          grow = __builtin_amdgcn_ballot_w64(g) != 0;
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf) cur[hf] = nxt[hf];
+          st_cur = st_next;
         }
       }
-      float mx = sv[0];
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the ring is quiet
+      __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();              // before the next piece refills it
+      // -- results ----------------------------------------------------------
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-      {
-        auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])) * sl2;
-      }
-      if (__builtin_amdgcn_ballot_w64(mx > m + kLazyRescaleLog2) != 0) {
-        rare_branch();
-        const float mnew = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - ((mnew == neg_inf()) ? 0.f : mnew));
-        l *= alpha;
+      for (int hf = 0; hf < H; ++hf) {
+        if (!ok[hf]) continue;
+        const int64_t orow = (int64_t)(r0 + jr[hf]) * a.num_q_heads + kvh * G + gr[hf];
+        if (npieces == 1) {
+          if (klim[hf] <= 0) continue;
+          const float inv = 1.f / l[hf];
+          uint16_t* out = static_cast<uint16_t*>(a.out) + orow * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        m = mnew;
-      }
-      const float nm = (m == neg_inf()) ? 0.f : -m;
-      float ps = 0.f;
-      bf16x8 pf[2];
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const uint32_t lo = f32_to_bf16_bits(o[hf][dt][4 * r4] * inv) |
+                                  ((uint32_t)f32_to_bf16_bits(o[hf][dt][4 * r4 + 1] * inv) << 16);
+              const uint32_t hi = f32_to_bf16_bits(o[hf][dt][4 * r4 + 2] * inv) |
+                                  ((uint32_t)f32_to_bf16_bits(o[hf][dt][4 * r4 + 3] * inv) << 16);
+              *reinterpret_cast<uint2*>(out + 32 * dt + 8 * r4 + 4 * h) = make_uint2(lo, hi);
+            }
+        } else if (slot < a.max_splits) {
+          const int64_t pidx = orow * a.max_splits + slot;
+          float* po = a.part_o + pidx * D;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sv[r], sl2, nm));
-        ps += p;
-        pf[r >> 3][r & 7] = static_cast<__bf16>(p);
-      }
-      {
-        auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
-        l += __uint_as_float(q[0]) + __uint_as_float(q[1]);
-      }
-      if (c + 32 > kv_wg) {
-        // keys past the last visible one may be unwritten slots
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (c + 16 * k2 + 8 * h + e >= kv_wg) vf[2 * dt + k2][e] = static_cast<__bf16>(0.f);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt + k2], pf[k2], o[dt], 0, 0, 0);
-    };
-
-    // Ring of NS stages: step i lives in stage i % NS and is loaded NS-1
-    // steps ahead.  Software pipeline: iteration i issues the S^T MFMAs of
-    // step i+1 before the softmax and PV of step i, so the matrix unit runs
-    // while the vector unit computes the exponentials.  Iteration i therefore
-    // waits for this wave's loads of step i+1 (those of step i+2 may stay in
-    // flight); the barrier then publishes every wave's loads and guarantees
-    // that all waves finished step i-1, whose stage the new loads (step
-    // i+NS-1) overwrite.  Loads past the end re-read the last step so that
-    // the count of loads in flight is the same in every iteration.
-    const int nsteps = (k_end - k_begin + 31) >> 5;
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p) dma(k_begin + 32 * min(p, nsteps - 1), p);
-    __builtin_amdgcn_s_waitcnt(0x3F70 | ((NS - 2) * DMA_PER_STEP));  // vmcnt: step 0 landed
-    __builtin_amdgcn_s_barrier();
-    f32x16 s_cur = wave_active ? scores(0) : f32x16{};
-    for (int i = 0; i < nsteps; ++i) {
-      __builtin_amdgcn_s_waitcnt(0x3F70 | ((NS - 3) * DMA_PER_STEP));  // vmcnt: step i+1 landed
-      __builtin_amdgcn_s_barrier();
-      dma(k_begin + 32 * min(i + NS - 1, nsteps - 1), (i + NS - 1) % NS);
-      if (wave_active) {
-        const f32x16 s_next = scores((i + 1) % NS);  // step i+1 (past the end: unused)
-        accumulate(s_cur, i % NS, k_begin + 32 * i);
-        s_cur = s_next;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): the ring is quiet
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();        // before the next item refills it
-
-    if (row_ok && klim > k_begin) {
-      const int ns = min((klim + ST - 1) / ST, a.max_splits);
-      const int64_t orow = (int64_t)(r0 + jrow) * a.num_q_heads + kvh * G + grow;
-      if (ns == 1) {
-        const float inv = 1.f / l;
-        uint16_t* out = static_cast<uint16_t*>(a.out) + orow * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            out[32 * dt + (r >> 2) * 8 + 4 * h + (r & 3)] = f32_to_bf16_bits(o[dt][r] * inv);
-      } else {
-        const int64_t pidx = orow * a.max_splits + split;
-        float* po = a.part_o + pidx * D;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) po[32 * dt + (r >> 2) * 8 + 4 * h + (r & 3)] = o[dt][r];
-        if (h == 0) {
-          a.part_ml[2 * pidx] = m;
-          a.part_ml[2 * pidx + 1] = l;
+            for (int r4 = 0; r4 < 4; ++r4)
+              *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * r4 + 4 * h) =
+                  f32x4{o[hf][dt][4 * r4], o[hf][dt][4 * r4 + 1], o[hf][dt][4 * r4 + 2],
+                        o[hf][dt][4 * r4 + 3]};
+          if (h == 0) {
+            a.part_ml[2 * pidx] = m[hf];
+            a.part_ml[2 * pidx + 1] = l[hf];
+          }
         }
+        if (a_step == 0 && h == 0) a.row_pieces[orow] = npieces;
       }
+
+      // -- next unit ----------------------------------------------------------
+      g += nsteps;
+      rem = 0;
+      if (!advance(tiles)) break;
     }
   }
 }
@@ -1585,9 +1735,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single)
   const int nblk = table_blocks(L, a.log2_block, a.max_blocks);
   const int kl = min(L - qn + j + 1, nblk << a.log2_block);
   if (kl <= 0) return;
-  const int ns = min((kl + a.split_tokens - 1) / a.split_tokens, a.max_splits);
-  if (ns <= 1) return;
   const int64_t orow = (int64_t)t * a.num_q_heads + h;
+  const int ns = min(a.row_pieces ? a.row_pieces[orow] : (kl + a.split_tokens - 1) / a.split_tokens,
+                     a.max_splits);
+  if (ns <= 1) return;
   const float* ml = a.part_ml + orow * a.max_splits * 2;
   const float* po = a.part_o + orow * a.max_splits * D;
   float acc[DD];
@@ -1664,10 +1815,11 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t st) {
   static thread_local Residency cache;
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
   int n = 0;
-  hipError_t err = resident(cache, prefill_kernel<D>, 256, lds, a.num_seqs, n);
+  hipError_t err =
+      resident(cache, prefill_kernel<D>, 64 * PrefillShape<D>::kWaves, lds, a.num_seqs, n);
   if (err != hipSuccess) return err;
   n = n >= 8 ? n / 8 * 8 : 8;  // the item walk deals runs of items to the 8 XCDs
-  prefill_kernel<D><<<n, 256, lds, st>>>(a, n);
+  prefill_kernel<D><<<n, 64 * PrefillShape<D>::kWaves, lds, st>>>(a, n);
   return hipGetLastError();
 }
 

@@ -60,14 +60,20 @@ def test_workspace_queries(lib):
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 100) == 0    # split not % 64
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 2048) > 0    # any multiple of 64
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 0, 16, 0) == 0
-    # chunked prefill: chunk rows get ceil(8704 / 2048) = 5 split slots each; the
+    # chunked prefill: chunk rows get max(ceil(8704 / 2048) = 5 fixed splits (vector-ALU
+    # path), ceil(272 steps / 91) + 1 = 4 stream-K pieces (MFMA path, ranges of at least
+    # ceil(272 / 3) = 91 steps)) = 5 slots each, plus an int32 piece count per row; the
     # balanced decode of single-token rows gets ceil(272 steps / 8) + 1 = 35 pieces
     # per (sequence, head) row; header 16 + 4 * 65 bytes rounded to 256.
     def al(x):
         return -(-x // 256) * 256
     assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 0) == \
-        al(2108 * 32 * 5 * 128 * 4) + al(2108 * 32 * 5 * 8) + al(64 * 32 * 35 * 128 * 4) + \
-        al(64 * 32 * 35 * 8) + 512
+        al(2108 * 32 * 5 * 128 * 4) + al(2108 * 32 * 5 * 8) + al(2108 * 32 * 4) + \
+        al(64 * 32 * 35 * 128 * 4) + al(64 * 32 * 35 * 8) + 512
+    # fixed ranges of 1024 keys (32 steps): ceil(272 / 32) + 1 = 10 slots per chunk row
+    assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 1024) == \
+        al(2108 * 32 * 10 * 128 * 4) + al(2108 * 32 * 10 * 8) + al(2108 * 32 * 4) + \
+        al(64 * 32 * 35 * 128 * 4) + al(64 * 32 * 35 * 8) + 512
     assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 96) == 0
 
 

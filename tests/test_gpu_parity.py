@@ -40,6 +40,19 @@ def test_split_counts_agree(split):
     assert err <= TOL[wl.shape.dtype]
 
 
+@pytest.mark.parametrize("split", [64, 256, 1024])
+def test_chunk_ranges_agree(split):
+    """Fixed ranges of `split` keys cut every row tile into many pieces; the
+    merged rows must agree with the oracle like the balanced default."""
+    shape = workloads.Shape("chunks", "bf16", 32, 8, 128, 16)
+    wl = workloads.make_workload(2, seed=91, device="cuda", seq_lens=[2100, 700, 5, 1300],
+                                 q_lens=[600, 700, 1, 64], shape=shape)
+    log(f"[chunk ranges] kv_split_tokens={split}")
+    out, err = run_and_compare(wl, kv_split_tokens=split, force_chunked=True)
+    log(f"[chunk ranges] max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 EDGE = [
     # dtype, Hq, Hkv, D, B, seq_lens, q_lens
     ("bf16", 32, 8, 128, 16, [1, 2, 15, 16, 17, 31, 32, 33], None),
@@ -62,6 +75,10 @@ EDGE = [
     ("bf16", 64, 8, 128, 16, [32768], None),                     # one long context, many pieces
     ("bf16", 32, 8, 128, 16, [5, 9000, 3, 1, 17000], None),      # ragged mix
     ("bf16", 32, 8, 64, 32, [4000, 70, 2500], None),             # head_dim 64, B = 32
+    ("bf16", 8, 2, 128, 8, [300, 90], [150, 2]),                 # chunks, B = 8
+    ("bf16", 8, 2, 128, 64, [700, 130], [300, 64]),              # chunks, B = 64
+    ("bf16", 8, 2, 64, 16, [500, 33], [257, 33]),                # chunks, head_dim 64, B = 16
+    ("bf16", 32, 8, 128, 16, [3000, 2500, 7], [1000, 700, 1]),   # long chunks, many row tiles
 ]
 
 
