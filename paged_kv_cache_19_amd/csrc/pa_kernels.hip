@@ -422,7 +422,7 @@ __device__ __forceinline__ int leading_shared_keys(const AttnArgs& a, const SeqV
 // Cache policy: with STREAM every K/V load is non-temporal (private blocks
 // are read once per call); without it loads go through the caches (shared
 // prefix blocks, and query chunks whose K/V several waves re-read).
-template <int D, int R, bool STREAM>
+template <int D, int R, bool STREAM, int NSETS = 2>
 __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int kv_wave, int kv_min,
                                        int k_begin, int k_end, RowState<D, R>& st) {
   constexpr int KK = D / 32;
@@ -536,21 +536,23 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
     }
   };
 
-  // Two fragment sets, loaded one step ahead.  The last prefetch re-reads
-  // the final step (an L2 hit) so that every iteration issues the same loads
-  // and the wait counts stay exact.
-  KVFrag<D> f0, f1;
-  int c = k_begin;
-  load(f0, c);
-  while (true) {
-    load(f1, c + 32 < k_end ? c + 32 : c);
-    compute(f0, c);
-    c += 32;
-    if (c >= k_end) break;
-    load(f0, c + 32 < k_end ? c + 32 : c);
-    compute(f1, c);
-    c += 32;
-    if (c >= k_end) break;
+  // A ring of NSETS fragment sets: the loads of step i + NSETS - 1 are
+  // issued before step i is computed, so NSETS - 1 steps are in flight while
+  // the wave computes.  Loads past the end re-read the final step (an L2
+  // hit) so that every step issues the same loads.
+  const int n = (k_end - k_begin + 31) >> 5;
+  auto step_key = [&](int i) { return k_begin + 32 * min(i, n - 1); };
+  KVFrag<D> f[NSETS];
+#pragma unroll
+  for (int p = 0; p < NSETS - 1; ++p) load(f[p], step_key(p));
+  for (int i0 = 0; i0 < n; i0 += NSETS) {
+#pragma unroll
+    for (int j = 0; j < NSETS; ++j) {
+      const int i = i0 + j;
+      if (i >= n) break;
+      load(f[(j + NSETS - 1) % NSETS], step_key(i + NSETS - 1));
+      compute(f[j], k_begin + 32 * i);
+    }
   }
 }
 
@@ -580,28 +582,27 @@ struct KVFrag8 {
   float ks, vs;        // scales of the block of the lane's 16 tokens
 };
 
-// Eight e4m3 codes (two dwords, lowest byte first) as bf16, exactly.
+// Eight e4m3 codes (two dwords, lowest byte first) as bf16, exactly: gfx950
+// converts a pair of fp8 codes straight to a pair of bf16 (with a unit
+// scale the result is the code's value; every e4m3 value is a bf16 value).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  bf16x8 r;
-  r[0] = static_cast<__bf16>(a[0]);
-  r[1] = static_cast<__bf16>(a[1]);
-  r[2] = static_cast<__bf16>(b[0]);
-  r[3] = static_cast<__bf16>(b[1]);
-  r[4] = static_cast<__bf16>(c[0]);
-  r[5] = static_cast<__bf16>(c[1]);
-  r[6] = static_cast<__bf16>(d[0]);
-  r[7] = static_cast<__bf16>(d[1]);
-  return r;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 __device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p, bool stream) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
   return stream ? __builtin_nontemporal_load(q) : *q;
 }
+
+// Fragment sets of the balanced-decode rings (steps in flight + 1); with
+// more than two sets the kernel runs one wave per SIMD (up to 512 registers).
+constexpr int kDecodeSets = 3;
+constexpr int kFp8Sets = 3;
 
 template <int D, bool STREAM>
 __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, int kv_wave,
@@ -654,13 +655,13 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
     f.vs = a.v_scales[(int64_t)bv * Hkv + v.kvh];
   };
 
-  // MASK: the step holds keys at or past kv_min (scores masked to -inf)
+  // mask: the step holds keys at or past kv_min (scores masked to -inf)
   // or kv_wave (V codes zeroed: they may be unwritten NaN slots).  Only the
-  // last step of a piece can; the others run without any per-key test.
-  auto compute = [&](KVFrag8<D>& f, int c, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // last step of a piece can; the tests sit behind a wave-uniform branch.
+  auto compute = [&](KVFrag8<D>& f, int c, bool mask) {
     const int pv = c + 16 * j4;
-    if constexpr (MASK) {
+    if (mask) {
+      rare_branch();
       // zero the V bytes of keys >= kv_wave (16 keys per lane, 4 per dword)
       const int nv = clampi(kv_wave - pv, 0, 16);
 #pragma unroll
@@ -689,7 +690,8 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[4 * x + r] = s4[x][r] * kscale;
-    if constexpr (MASK) {
+    if (mask) {
+      rare_branch();
       const int lim = st.klim[0] - pv;
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[e] = (e < lim) ? sv[e] : neg_inf();
@@ -733,30 +735,25 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
   };
 
   // Steps below k_safe need no mask; at most one step (the last) does.
-  // Two fragment sets, loaded one step ahead (the last prefetch re-reads the
-  // final step so that every iteration issues the same loads).
+  // A ring of kFp8Sets fragment sets: the loads of step i + kFp8Sets - 1 are
+  // issued before step i is computed, so kFp8Sets - 1 steps are in flight
+  // while the wave computes (loads past the end re-read the final step so
+  // that every step issues the same loads).
   const int k_safe = max(k_begin, min(k_end, (min(kv_min, kv_wave) - k_begin) / 64 * 64 + k_begin));
-  KVFrag8<D> f0, f1;
-  int c = k_begin;
-  if (c < k_safe) {
-    load(f0, c);
-    while (true) {
-      load(f1, c + 64 < k_end ? c + 64 : c);
-      compute(f0, c, std::false_type());
-      c += 64;
-      if (c >= k_safe) break;
-      load(f0, c + 64 < k_end ? c + 64 : c);
-      compute(f1, c, std::false_type());
-      c += 64;
-      if (c >= k_safe) {
-        f1 = f0;
-        break;
-      }
+  const int n = (k_end - k_begin + 63) >> 6;
+  auto step_key = [&](int i) { return k_begin + 64 * min(i, n - 1); };
+  KVFrag8<D> f[kFp8Sets];
+#pragma unroll
+  for (int p = 0; p < kFp8Sets - 1; ++p) load(f[p], step_key(p));
+  for (int i0 = 0; i0 < n; i0 += kFp8Sets) {
+#pragma unroll
+    for (int j = 0; j < kFp8Sets; ++j) {
+      const int i = i0 + j;
+      if (i >= n) break;
+      load(f[(j + kFp8Sets - 1) % kFp8Sets], step_key(i + kFp8Sets - 1));
+      const int c = k_begin + 64 * i;
+      compute(f[j], c, c + 64 > k_safe);
     }
-    if (c < k_end) compute(f1, c, std::true_type());  // prefetched by the last iteration
-  } else if (c < k_end) {
-    load(f1, c);
-    compute(f1, c, std::true_type());
   }
 }
 
@@ -905,7 +902,9 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t g, int64_t waves, int64_
 // FP8: the cache is e4m3 with per-(block, KV head) scales and a step is 64
 // keys (the bf16 cache steps 32 keys at a time).
 template <int D, bool FP8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_streamk_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2, (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2)))
+void decode_streamk_kernel(
     AttnArgs a, int waves, StreamKHeader* hdr) {
   constexpr int STEP = FP8 ? 64 : 32;
   constexpr int LSTEP = FP8 ? 6 : 5;
@@ -997,9 +996,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       if (k_end > max(k_begin, k_sh))
         attend_fp8<D, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     } else {
-      if (k_sh > k_begin) attend<D, 1, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+      if (k_sh > k_begin)
+        attend<D, 1, false, kDecodeSets>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
       if (k_end > max(k_begin, k_sh))
-        attend<D, 1, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+        attend<D, 1, true, kDecodeSets>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     }
     write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
                      PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
