@@ -41,10 +41,6 @@ struct AttnArgs {
 // steps, which bounds the pieces one row can be cut into.
 constexpr int kMinStepsPerWave = 8;
 
-// Which sequences a launch serves (chunked prefill runs a wide-tile kernel
-// for chunks and a narrow one for single-token rows).
-enum RowFilter : int32_t { kAllSeqs = 0, kMultiRowSeqs = 1, kSingleRowSeqs = 2 };
-
 hipError_t launch_slot_mapping(int64_t* slots, const int32_t* bt, int32_t max_blocks,
                                const int32_t* seq_lens, const int32_t* qsl,
                                int32_t num_seqs, int32_t num_tokens, int32_t block_size,

@@ -10,14 +10,21 @@
 // side").
 //
 // Kernels
-//   slot_mapping_kernel       slot of every query token (index equations)
-//   reshape_and_cache_kernel  bit copy of new K/V into their slots
-//   attn_mfma_kernel<D, R>    bf16 split-K attention; QK^T and PV on
-//                             v_mfma_f32_16x16x32_bf16, online softmax in
-//                             fp32 with cross-lane max/sum
-//   attn_valu_kernel<ES, D>   fp32 (and small-block bf16) split-K attention
-//                             on the vector ALUs
-//   merge_kernel<ES, D>       exact log-sum-exp merge of split partials
+//   slot_mapping_kernel          slot of every query token (index equations)
+//   reshape_and_cache_kernel     bit copy of new K/V into their slots
+//   reshape_and_cache_fp8_kernel the same into e4m3 pools (per-block scales)
+//   copy_blocks_kernel           whole-block copies (copy-on-write, swap)
+//   decode_streamk_kernel<D, FP8> balanced split-K decode (bf16 or e4m3
+//                                cache); QK^T and PV on
+//                                v_mfma_f32_16x16x32_bf16, online softmax in
+//                                fp32 with cross-lane max/sum
+//   merge_streamk_kernel         log-sum-exp merge of its pieces
+//   prefill_kernel<D>            causal query chunks on
+//                                v_mfma_f32_32x32x16_bf16, K/V staged in LDS
+//   attn_mfma_kernel<D>          fixed-split bf16 decode
+//   attn_valu_kernel<ES, D>      fp32 (and small-block bf16) split-K attention
+//                                on the vector ALUs
+//   merge_kernel<ES, D>          exact log-sum-exp merge of split partials
 //
 // Cache layout: K [NB, Hkv, B, D] (token rows), V [NB, Hkv, D, B] (each
 // head_dim row holds the block's tokens).  The V layout lets one 16-byte
@@ -827,12 +834,13 @@ __device__ __forceinline__ void write_rows(const AttnArgs& a, const SeqView& v, 
 }
 
 // ---------------------------------------------------------------------------
-// Fixed-split bf16 attention: one wave per (sequence x KV head, row-tile
-// group, split of split_tokens keys).  Serves query chunks (R = 2) and
-// decode rows when a split size is given.
+// Fixed-split bf16 decode: one wave per (sequence x KV head, 16-row tile of
+// the G query heads, split of split_tokens keys).  pa_decode runs it when a
+// split size is given (kv_split_tokens > 0).
 // ---------------------------------------------------------------------------
-template <int D, int R>
-__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
+template <int D>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int R = 1;
   // Grid: x = (sequence, KV head) fastest, z = split.  Workgroups are dealt
   // to the 8 XCDs round-robin by linear id, so this gives every XCD the same
   // mix of sequences and splits (with the split fastest, XCD k would get
@@ -845,8 +853,6 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
   const int L = a.seq_lens[s];
   int r0, qn;
   seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-  if (filter == kMultiRowSeqs && qn <= 1) return;
-  if (filter == kSingleRowSeqs && qn != 1) return;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int nrows = qn * G;
   const int row0 = tg * 16 * R;
@@ -862,16 +868,12 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a, int filter) {
   const int k_end = min(k_begin + a.split_tokens, kv_wave);
   RowState<D, R> st;
   load_rows<D, R>(a, v, row0, st);
-  if (R == 1) {
-    // Single-tile waves (decode rows) are the only readers of their K/V:
-    // stream it, except the leading shared blocks.
-    const int k_sh = k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) : 0;
-    if (k_sh > k_begin) attend<D, R, false>(a, v, kv_wave, kv_min, k_begin, min(k_sh, k_end), st);
-    if (k_end > max(k_begin, k_sh))
-      attend<D, R, true>(a, v, kv_wave, kv_min, max(k_begin, k_sh), k_end, st);
-  } else {
-    attend<D, R, false>(a, v, kv_wave, kv_min, k_begin, k_end, st);
-  }
+  // A decode wave is the only reader of its K/V: stream it, except the
+  // leading shared blocks.
+  const int k_sh = k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) : 0;
+  if (k_sh > k_begin) attend<D, R, false>(a, v, kv_wave, kv_min, k_begin, min(k_sh, k_end), st);
+  if (k_end > max(k_begin, k_sh))
+    attend<D, R, true>(a, v, kv_wave, kv_min, max(k_begin, k_sh), k_end, st);
   // A row whose keys span more than one split leaves a partial in slot
   // ``split`` for the merge pass; the others are final here.
   write_rows<D, R>(a, v, row0, st, false, split, PartialDst{a.part_o, a.part_ml, a.max_splits, -1},
@@ -1846,7 +1848,7 @@ hipError_t launch_mfma(const AttnArgs& a, bool has_chunks, void* header, hipStre
   const int G = a.num_q_heads / a.num_kv_heads;
   const unsigned z = (unsigned)a.num_seqs * a.num_kv_heads;
   const unsigned narrow_tiles = (unsigned)((G + 15) / 16);
-  attn_mfma_kernel<D, 1><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a, kAllSeqs);
+  attn_mfma_kernel<D><<<dim3(z, narrow_tiles, a.max_splits), 64, 0, st>>>(a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   return a.max_splits > 1 ? launch_merge<2, D>(a, 0, st) : hipSuccess;
