@@ -80,6 +80,9 @@ hipError_t launch_attention(const AttnArgs& a, bool has_chunks, void* header,
 // Largest batch the persistent chunk kernel takes (its per-sequence item
 // prefix sums live in LDS).
 constexpr int kMaxChunkSeqs = 2048;
+// Largest batch whose chunk units and decode rows share one launch (both
+// kinds of prefix sums sit next to the chunk kernel's LDS ring).
+constexpr int kMaxMixSeqs = 1024;
 
 // Balanced ("stream-K") decode over a fixed set of resident waves, then the
 // merge of the pieces (bf16 or, with a.kv_fp8, e4m3 cache).  ``header`` is workspace for the step prefix sums

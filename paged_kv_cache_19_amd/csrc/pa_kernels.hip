@@ -903,22 +903,16 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t g, int64_t waves, int64_
 
 // FP8: the cache is e4m3 with per-(block, KV head) scales and a step is 64
 // keys (the bf16 cache steps 32 keys at a time).
-template <int D, bool FP8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
-    (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2, (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2)))
-void decode_streamk_kernel(
-    AttnArgs a, int waves, StreamKHeader* hdr) {
+// Decode steps (per KV head) of every sequence's single-token rows in
+// P[s + 1] and the lengths in Ls[s], by nthreads threads; the caller
+// synchronises before the scan.
+template <bool FP8>
+__device__ __forceinline__ void decode_prefix_fill(const AttnArgs& a, int* P, int* Ls, int tid,
+                                                   int nthreads) {
   constexpr int STEP = FP8 ? 64 : 32;
   constexpr int LSTEP = FP8 ? 6 : 5;
-  extern __shared__ int smem[];
-  const int S = a.num_seqs;
-  int* P = smem;           // [S + 1] steps before sequence s (per KV head)
-  int* Ls = smem + S + 1;  // [S]     sequence lengths
-  const int lane = threadIdx.x;
-  const int w = blockIdx.x;
-  const int Hkv = a.num_kv_heads;
   const int lg = a.log2_block;
-  for (int s = lane; s < S; s += 64) {
+  for (int s = tid; s < a.num_seqs; s += nthreads) {
     const int L = a.seq_lens[s];
     int r0, qn;
     seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
@@ -927,41 +921,39 @@ void decode_streamk_kernel(
     P[s + 1] = (qn == 1 && kl > 0) ? (kl + STEP - 1) >> LSTEP : 0;
     Ls[s] = L;
   }
-  __syncthreads();
-  {
-    const int k = (S + 63) >> 6;
-    const int lo = min(lane * k, S);
-    const int hi = min(lo + k, S);
-    int run = 0;
-    for (int s = lo; s < hi; ++s) {
-      run += P[s + 1];
-      P[s + 1] = run;
-    }
-    int incl = run;
+}
+
+// In-place prefix sums of P[1..S] (P[0] = 0) by the 64 lanes of one wave.
+__device__ __forceinline__ void decode_prefix_scan(int* P, int S, int lane) {
+  const int k = (S + 63) >> 6;
+  const int lo = min(lane * k, S);
+  const int hi = min(lo + k, S);
+  int run = 0;
+  for (int s = lo; s < hi; ++s) {
+    run += P[s + 1];
+    P[s + 1] = run;
+  }
+  int incl = run;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    const int off = incl - run;
-    for (int s = lo; s < hi; ++s) P[s + 1] += off;
-    if (lane == 0) P[0] = 0;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
   }
-  __syncthreads();
-  const int64_t N = (int64_t)Hkv * P[S];
-  const int64_t weff = N == 0 ? 0 : min((int64_t)waves, max((int64_t)1, N / kMinStepsPerWave));
-  if (w == 0) {
-    if (lane == 0) {
-      hdr->total_steps = N;
-      hdr->waves = weff;
-    }
-    int* hp = reinterpret_cast<int*>(hdr + 1);
-    for (int s = lane; s <= S; s += 64) hp[s] = P[s];
-  }
-  if (w >= weff) return;
+  const int off = incl - run;
+  for (int s = lo; s < hi; ++s) P[s + 1] += off;
+  if (lane == 0) P[0] = 0;
+}
+
+// Wave w's share (of weff) of the N decode steps, given the step prefix sums
+// P and lengths Ls; NSETS fragment sets in the bf16 ring.
+template <int D, bool FP8, int NSETS>
+__device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, const int* Ls,
+                                             int64_t N, int64_t weff, int w) {
+  constexpr int STEP = FP8 ? 64 : 32;
+  const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
   int64_t g = (int64_t)w * N / weff;
   const int64_t g_end = (int64_t)(w + 1) * N / weff;
-
   // Sequence holding step g: the largest s with Hkv * P[s] <= g.
   int s;
   {
@@ -999,14 +991,43 @@ void decode_streamk_kernel(
         attend_fp8<D, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     } else {
       if (k_sh > k_begin)
-        attend<D, 1, false, kDecodeSets>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+        attend<D, 1, false, NSETS>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
       if (k_end > max(k_begin, k_sh))
-        attend<D, 1, true, kDecodeSets>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+        attend<D, 1, true, NSETS>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     }
     write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
                      PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
     g += c1 - c0;
   }
+}
+
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2, (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2)))
+void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
+  extern __shared__ int smem[];
+  const int S = a.num_seqs;
+  int* P = smem;           // [S + 1] steps before sequence s (per KV head)
+  int* Ls = smem + S + 1;  // [S]     sequence lengths
+  const int lane = threadIdx.x;
+  const int w = blockIdx.x;
+  decode_prefix_fill<FP8>(a, P, Ls, lane, 64);
+  __syncthreads();
+  decode_prefix_scan(P, S, lane);
+  __syncthreads();
+  const int64_t N = (int64_t)a.num_kv_heads * P[S];
+  const int64_t weff = N == 0 ? 0 : min((int64_t)waves, max((int64_t)1, N / kMinStepsPerWave));
+  if (w == 0) {
+    if (lane == 0) {
+      hdr->total_steps = N;
+      hdr->waves = weff;
+    }
+    int* hp = reinterpret_cast<int*>(hdr + 1);
+    for (int s = lane; s <= S; s += 64) hp[s] = P[s];
+  }
+  if (w >= weff) return;
+  decode_share<D, FP8, kDecodeSets>(a, P, Ls, N, weff, w);
 }
 
 // Merge for the balanced decode: the pieces of row (s, h) are the waves whose
@@ -1165,10 +1186,30 @@ __device__ __forceinline__ int seq_unit_steps(const AttnArgs& a, int s, int G, i
   return n;
 }
 
+// Steps per sequence (all KV heads) of the chunk units, then their prefix
+// sums: seq_prefix[s] = steps before sequence s.  All threads of the
+// workgroup take part; ends synchronised.
 template <int D>
-__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
-    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
-void prefill_kernel(AttnArgs a, int num_wgs) {
+__device__ __forceinline__ void prefill_prefix(const AttnArgs& a, int* seq_prefix) {
+  constexpr int NW = PrefillShape<D>::kWaves;
+  const int tid = threadIdx.x;
+  const int S = a.num_seqs;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  for (int s = tid; s < S; s += 64 * NW)
+    seq_prefix[s + 1] = a.num_kv_heads * seq_unit_steps(a, s, G, PrefillShape<D>::kRows);
+  __syncthreads();
+  if (tid == 0) {
+    seq_prefix[0] = 0;
+    for (int s = 0; s < S; ++s) seq_prefix[s + 1] += seq_prefix[s];
+  }
+  __syncthreads();
+}
+
+// The chunk units' work of workgroup wg of num_wgs (a multiple of 8), given
+// the step prefix sums.  Every wave of the workgroup takes part (barriers).
+template <int D>
+__device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq_prefix, int wg,
+                                               int num_wgs) {
   constexpr int H = PrefillShape<D>::kHalves;    // 32-row halves per wave
   constexpr int NW = PrefillShape<D>::kWaves;
   constexpr int ROWS = PrefillShape<D>::kRows;
@@ -1182,7 +1223,6 @@ void prefill_kernel(AttnArgs a, int num_wgs) {
   constexpr int GS = kPrefillGroup;
   constexpr int TILE = 32 * D;                   // elements of one K or V^T tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[NS][2][TILE];
-  extern __shared__ int seq_prefix[];            // [num_seqs + 1] steps
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // known wave-uniform
@@ -1197,19 +1237,10 @@ void prefill_kernel(AttnArgs a, int num_wgs) {
   const int cpb = Bs >> 3;       // 8-key chunks of one block inside a step (1, 2, 4)
   const int lcpb = cpb == 4 ? 2 : cpb - 1;
 
-  // Steps per sequence (all KV heads), then their prefix sums.
-  for (int s = tid; s < S; s += 64 * NW) seq_prefix[s + 1] = Hkv * seq_unit_steps(a, s, G, ROWS);
-  __syncthreads();
-  if (tid == 0) {
-    seq_prefix[0] = 0;
-    for (int s = 0; s < S; ++s) seq_prefix[s + 1] += seq_prefix[s];
-  }
-  __syncthreads();
   const int N = seq_prefix[S];
   if (N == 0) return;
   const int chunk = a.chunk_auto ? max((N + num_wgs - 1) / num_wgs, a.chunk_steps) : a.chunk_steps;
   const int nranges = (N + chunk - 1) / chunk;
-  const int wg = blockIdx.x;
 
   // Per-lane pieces of the load and read addresses, fixed for the kernel.
   int k_voff[IPW], v_voff[IPW], v_bi[IPW];
@@ -1581,6 +1612,87 @@ void prefill_kernel(AttnArgs a, int num_wgs) {
   }
 }
 
+
+template <int D>
+__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
+    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
+void prefill_kernel(AttnArgs a, int num_wgs) {
+  extern __shared__ int seq_prefix[];  // [num_seqs + 1] steps
+  prefill_prefix<D>(a, seq_prefix);
+  prefill_ranges<D>(a, seq_prefix, blockIdx.x, num_wgs);
+}
+
+// Chunk units and single-token rows of one call in one persistent launch:
+// the resident workgroups are split between the two kinds of work, so that
+// the matrix-bound chunk units and the memory-bound decode rows run at the
+// same time on different CUs instead of one after the other.  Every
+// workgroup builds both step prefix sums and derives the same split from
+// them: the CUs are shared in proportion to the estimated CU-time of each
+// kind (kChunkStepNs per 256-row chunk step, kDecodeStepNs per 32-key decode
+// step), in multiples of 8 so that every XCD gets the same mix.  Chunk
+// workgroups run prefill_ranges; each wave of a decode workgroup is one wave
+// of the balanced decode (two fragment sets, so that both kinds fit the same
+// 256-register budget).
+// Relative CU-time per step (D = 128; half at D = 64).  A chunk step
+// (256 rows x 32 keys) takes ~1.49 us of a CU; the decode cost is the value
+// at which the chunked-prefill mix (4 x 512-token chunks + 60 decode rows)
+// ran fastest over a sweep of 410..2000 (it is worth more than its bytes at
+// the HBM rate: a CU streams far below its share of HBM bandwidth).
+constexpr int64_t kChunkStepNs = 1490;
+constexpr int64_t kDecodeStepNs = 700;
+
+template <int D>
+__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
+    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
+void chunk_mix_kernel(AttnArgs a, int num_wgs, StreamKHeader* hdr) {
+  constexpr int NW = PrefillShape<D>::kWaves;
+  static_assert(PrefillShape<D>::kHalves == 1, "decode waves need the two-wave register budget");
+  extern __shared__ int lds_i[];
+  const int S = a.num_seqs;
+  int* seq_prefix = lds_i;        // [S + 1] chunk steps before sequence s
+  int* P = lds_i + S + 1;         // [S + 1] decode steps before sequence s (per KV head)
+  int* Ls = P + S + 1;            // [S]     sequence lengths
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  decode_prefix_fill<false>(a, P, Ls, tid, 64 * NW);
+  prefill_prefix<D>(a, seq_prefix);  // synchronises: P and Ls are filled too
+  if (w == 0) decode_prefix_scan(P, S, lane);
+  __syncthreads();
+  const int64_t n_pf = seq_prefix[S];
+  const int64_t n_dec = (int64_t)a.num_kv_heads * P[S];
+  int w_dec = 0;
+  if (n_dec > 0) {
+    const int64_t pf = n_pf * (kChunkStepNs * D / 128);
+    const int64_t dec = n_dec * (kDecodeStepNs * D / 128);
+    w_dec = (int)(((int64_t)num_wgs * dec / (pf + dec) + 4) / 8 * 8);
+    w_dec = max(w_dec, 8);
+    if (n_pf > 0) w_dec = min(w_dec, num_wgs - 8);
+  }
+  const int w_pf = num_wgs - w_dec;
+  if ((int)blockIdx.x < w_pf) {
+    if (w_dec == 0 && blockIdx.x == 0 && tid == 0) {  // no decode rows: an empty header
+      hdr->total_steps = 0;
+      hdr->waves = 0;
+    }
+    prefill_ranges<D>(a, seq_prefix, blockIdx.x, w_pf);
+    return;
+  }
+  const int64_t waves = (int64_t)w_dec * NW;
+  const int64_t weff = n_dec == 0 ? 0 : min(waves, max((int64_t)1, n_dec / kMinStepsPerWave));
+  const int dw = (blockIdx.x - w_pf) * NW + w;
+  if (dw == 0) {
+    if (lane == 0) {
+      hdr->total_steps = n_dec;
+      hdr->waves = weff;
+    }
+    int* hp = reinterpret_cast<int*>(hdr + 1);
+    for (int s = lane; s <= S; s += 64) hp[s] = P[s];
+  }
+  if (dw >= weff) return;
+  decode_share<D, false, 2>(a, P, Ls, n_dec, weff, dw);
+}
+
 // ---------------------------------------------------------------------------
 // Vector-ALU attention: one wave per (query token, KV head, split) serving
 // the G heads of the group.  Lanes own keys for QK^T and head_dim columns for
@@ -1825,6 +1937,24 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Chunk units and decode rows together (chunk_mix_kernel), then the merges.
+template <int D>
+hipError_t launch_mix(const AttnArgs& a, void* header, hipStream_t st) {
+  static thread_local Residency cache;
+  const size_t lds = (size_t)(3 * a.num_seqs + 2) * sizeof(int);
+  int n = 0;
+  hipError_t err =
+      resident(cache, chunk_mix_kernel<D>, 64 * PrefillShape<D>::kWaves, lds, a.num_seqs, n);
+  if (err != hipSuccess) return err;
+  n = n >= 16 ? n / 8 * 8 : 16;  // both kinds of work get whole multiples of 8
+  StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
+  chunk_mix_kernel<D><<<n, 64 * PrefillShape<D>::kWaves, lds, st>>>(a, n, hdr);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  merge_streamk_kernel<2, D><<<dim3((a.num_q_heads + 3) / 4, a.num_seqs), 256, 0, st>>>(a, hdr);
+  return hipGetLastError();
+}
+
 template <int ES, int D>
 hipError_t launch_merge(const AttnArgs& a, int skip_single, hipStream_t st) {
   merge_kernel<ES, D><<<dim3((a.num_q_heads + 3) / 4, a.num_tokens), 256, 0, st>>>(a, skip_single);
@@ -1836,12 +1966,17 @@ hipError_t launch_mfma(const AttnArgs& a, bool has_chunks, void* header, hipStre
   hipError_t err;
   if (has_chunks) {
     // Query chunks on the persistent chunk kernel, single-token rows on the
-    // balanced decode; then the merge of split chunk rows.
-    if (a.max_query_len > 1) {
-      err = launch_prefill<D>(a, st);
-      if (err != hipSuccess) return err;
+    // balanced decode -- both in one launch when the prefix sums fit next to
+    // the LDS ring -- then the merge of split chunk rows.
+    if (a.max_query_len > 1 && a.num_seqs <= kMaxMixSeqs) {
+      err = launch_mix<D>(a, header, st);
+    } else {
+      if (a.max_query_len > 1) {
+        err = launch_prefill<D>(a, st);
+        if (err != hipSuccess) return err;
+      }
+      err = launch_streamk<D>(a, header, st);
     }
-    err = launch_streamk<D>(a, header, st);
     if (err != hipSuccess) return err;
     return a.max_splits > 1 ? launch_merge<2, D>(a, 1, st) : hipSuccess;
   }
