@@ -545,19 +545,19 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
 
   // A ring of NSETS fragment sets: the loads of step i + NSETS - 1 are
   // issued before step i is computed, so NSETS - 1 steps are in flight while
-  // the wave computes.  Loads past the end re-read the final step (an L2
-  // hit) so that every step issues the same loads.
+  // the wave computes.  Steps past the end are not loaded (a wave-uniform
+  // test; the waits are the compiler's, on the registers each step reads).
   const int n = (k_end - k_begin + 31) >> 5;
-  auto step_key = [&](int i) { return k_begin + 32 * min(i, n - 1); };
   KVFrag<D> f[NSETS];
 #pragma unroll
-  for (int p = 0; p < NSETS - 1; ++p) load(f[p], step_key(p));
+  for (int p = 0; p < NSETS - 1; ++p)
+    if (p < n) load(f[p], k_begin + 32 * p);
   for (int i0 = 0; i0 < n; i0 += NSETS) {
 #pragma unroll
     for (int j = 0; j < NSETS; ++j) {
       const int i = i0 + j;
       if (i >= n) break;
-      load(f[(j + NSETS - 1) % NSETS], step_key(i + NSETS - 1));
+      if (i + NSETS - 1 < n) load(f[(j + NSETS - 1) % NSETS], k_begin + 32 * (i + NSETS - 1));
       compute(f[j], k_begin + 32 * i);
     }
   }
@@ -744,20 +744,19 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
   // Steps below k_safe need no mask; at most one step (the last) does.
   // A ring of kFp8Sets fragment sets: the loads of step i + kFp8Sets - 1 are
   // issued before step i is computed, so kFp8Sets - 1 steps are in flight
-  // while the wave computes (loads past the end re-read the final step so
-  // that every step issues the same loads).
+  // while the wave computes; steps past the end are not loaded.
   const int k_safe = max(k_begin, min(k_end, (min(kv_min, kv_wave) - k_begin) / 64 * 64 + k_begin));
   const int n = (k_end - k_begin + 63) >> 6;
-  auto step_key = [&](int i) { return k_begin + 64 * min(i, n - 1); };
   KVFrag8<D> f[kFp8Sets];
 #pragma unroll
-  for (int p = 0; p < kFp8Sets - 1; ++p) load(f[p], step_key(p));
+  for (int p = 0; p < kFp8Sets - 1; ++p)
+    if (p < n) load(f[p], k_begin + 64 * p);
   for (int i0 = 0; i0 < n; i0 += kFp8Sets) {
 #pragma unroll
     for (int j = 0; j < kFp8Sets; ++j) {
       const int i = i0 + j;
       if (i >= n) break;
-      load(f[(j + kFp8Sets - 1) % kFp8Sets], step_key(i + kFp8Sets - 1));
+      if (i + kFp8Sets - 1 < n) load(f[(j + kFp8Sets - 1) % kFp8Sets], k_begin + 64 * (i + kFp8Sets - 1));
       const int c = k_begin + 64 * i;
       compute(f[j], c, c + 64 > k_safe);
     }
