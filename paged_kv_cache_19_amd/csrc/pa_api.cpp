@@ -82,7 +82,7 @@ bool plan_workspace(int num_tokens, int num_seqs, int num_q_heads, int head_dim,
   p->split_tokens = st;
   p->max_splits = (max_seq_len + st - 1) / st;
   const int steps = (max_seq_len + 31) / 32;
-  p->max_pieces = (steps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
+  p->max_pieces = (steps + pa::kPieceCostSteps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
   const size_t ob = (size_t)head_dim * sizeof(float), mlb = 2 * sizeof(float);
   if (chunk_entry) {
     // The chunk kernel cuts each row tile's steps into at most

@@ -40,6 +40,10 @@ struct AttnArgs {
 // Balanced decode: every resident wave streams at least this many 32-key
 // steps, which bounds the pieces one row can be cut into.
 constexpr int kMinStepsPerWave = 8;
+// Work-list cost of starting a piece (query rows, block-table window, ring
+// fill), in steps: each (sequence, KV head) item costs its steps plus this,
+// so waves whose share crosses more items get fewer steps.
+constexpr int kPieceCostSteps = 3;
 
 hipError_t launch_slot_mapping(int64_t* slots, const int32_t* bt, int32_t max_blocks,
                                const int32_t* seq_lens, const int32_t* qsl,

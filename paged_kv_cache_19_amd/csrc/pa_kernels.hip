@@ -917,7 +917,8 @@ __device__ __forceinline__ void decode_prefix_fill(const AttnArgs& a, int* P, in
     seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
     const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
     // Only single-token rows are decode work (query chunks have their own kernel).
-    P[s + 1] = (qn == 1 && kl > 0) ? (kl + STEP - 1) >> LSTEP : 0;
+    // An item's cost is its steps plus kPieceCostSteps for starting a piece.
+    P[s + 1] = (qn == 1 && kl > 0) ? ((kl + STEP - 1) >> LSTEP) + kPieceCostSteps : 0;
     Ls[s] = L;
   }
 }
@@ -966,12 +967,15 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
   }
   while (g < g_end) {
     while ((int64_t)Hkv * P[s + 1] <= g) ++s;
-    const int nch = P[s + 1] - P[s];
+    const int cost = P[s + 1] - P[s];  // steps + kPieceCostSteps
+    const int nch = cost - kPieceCostSteps;
     const int64_t base = (int64_t)Hkv * P[s];
-    const int kvh = (int)((g - base) / nch);
-    const int c0 = (int)(g - base - (int64_t)kvh * nch);
-    const int c1 = (int)min((int64_t)nch, c0 + (g_end - g));
-    const int64_t g_item = base + (int64_t)kvh * nch;
+    const int kvh = (int)((g - base) / cost);
+    const int64_t g_item = base + (int64_t)kvh * cost + kPieceCostSteps;  // the item's step 0
+    const int c0 = (int)max((int64_t)0, g - g_item);
+    const int c1 = (int)min((int64_t)nch, g_end - g_item);
+    g = g_item + nch;  // next item (or past g_end)
+    if (c1 <= c0) continue;  // the share holds only the start-up cost of this item
     const int64_t wf = wave_of_step(g_item, weff, N);
     const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
     int r0, qn;
@@ -996,7 +1000,6 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     }
     write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
                      PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
-    g += c1 - c0;
   }
 }
 
@@ -1043,11 +1046,13 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   const int64_t weff = hdr->waves;
   if (N <= 0 || weff <= 0) return;
   const int* P = reinterpret_cast<const int*>(hdr + 1);
-  const int nch = P[s + 1] - P[s];
-  if (nch <= 0) return;
+  const int cost = P[s + 1] - P[s];
+  if (cost <= 0) return;
+  const int nch = cost - kPieceCostSteps;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int kvh = h / G;
-  const int64_t g_item = (int64_t)a.num_kv_heads * P[s] + (int64_t)kvh * nch;
+  const int64_t g_item =
+      (int64_t)a.num_kv_heads * P[s] + (int64_t)kvh * cost + kPieceCostSteps;
   const int64_t wf = wave_of_step(g_item, weff, N);
   const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
   const int ns = (int)min(wl - wf + 1, (int64_t)a.sk_slots);

@@ -51,10 +51,11 @@ def test_workspace_queries(lib):
     splits = 16
     # partials (o then (m, l), fp32) plus a header of 16 + 4 * (128 + 1) bytes rounded to 256
     assert n == 128 * 64 * splits * 128 * 4 + 128 * 64 * splits * 2 * 4 + 768
-    # balanced decode (split 0): up to ceil(256 steps / 8) + 1 = 33 pieces per row,
+    # balanced decode (split 0): a row's 256 steps plus the 3-step start-up cost of a
+    # piece, cut into shares of at least 8: up to ceil(259 / 8) + 1 = 34 pieces per row,
     # plus a header of 16 + 4 * (128 + 1) bytes rounded to 256
     assert lib.pa_decode_workspace_bytes(128, 64, 128, 8192, 16, 0) == \
-        128 * 64 * 33 * 128 * 4 + 128 * 64 * 33 * 2 * 4 + 768
+        128 * 64 * 34 * 128 * 4 + 128 * 64 * 34 * 2 * 4 + 768
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 4, 0) > 0
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 3, 0) == 0       # B not a power of 2
     assert lib.pa_decode_workspace_bytes(4, 8, 64, 64, 16, 100) == 0    # split not % 64
@@ -63,17 +64,17 @@ def test_workspace_queries(lib):
     # chunked prefill: chunk rows get max(ceil(8704 / 2048) = 5 fixed splits (vector-ALU
     # path), ceil(272 steps / 91) + 1 = 4 stream-K pieces (MFMA path, ranges of at least
     # ceil(272 / 3) = 91 steps)) = 5 slots each, plus an int32 piece count per row; the
-    # balanced decode of single-token rows gets ceil(272 steps / 8) + 1 = 35 pieces
+    # balanced decode of single-token rows gets ceil((272 + 3) / 8) + 1 = 36 pieces
     # per (sequence, head) row; header 16 + 4 * 65 bytes rounded to 256.
     def al(x):
         return -(-x // 256) * 256
     assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 0) == \
         al(2108 * 32 * 5 * 128 * 4) + al(2108 * 32 * 5 * 8) + al(2108 * 32 * 4) + \
-        al(64 * 32 * 35 * 128 * 4) + al(64 * 32 * 35 * 8) + 512
+        al(64 * 32 * 36 * 128 * 4) + al(64 * 32 * 36 * 8) + 512
     # fixed ranges of 1024 keys (32 steps): ceil(272 / 32) + 1 = 10 slots per chunk row
     assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 1024) == \
         al(2108 * 32 * 10 * 128 * 4) + al(2108 * 32 * 10 * 8) + al(2108 * 32 * 4) + \
-        al(64 * 32 * 35 * 128 * 4) + al(64 * 32 * 35 * 8) + 512
+        al(64 * 32 * 36 * 128 * 4) + al(64 * 32 * 36 * 8) + 512
     assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 96) == 0
 
 
