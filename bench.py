@@ -293,8 +293,9 @@ def main():
         f_chunk, f_single = algorithmic_flops(wl)
         achieved = (f_chunk + f_single) / (attn_avg * 1e-3) / 1e12
         roofline = {
-            "kernel": "pa_chunked_prefill: persistent query-chunk kernel (MFMA) + balanced "
-                      "decode of the single-token rows + merges",
+            "kernel": "pa_chunked_prefill: one persistent launch splitting the CUs between the "
+                      "query-chunk units (MFMA) and the balanced decode of the single-token "
+                      "rows, then the merges",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
