@@ -53,6 +53,20 @@ def test_chunk_ranges_agree(split):
     assert err <= TOL["bf16"]
 
 
+def test_chunks_beyond_one_launch():
+    """More sequences than the fused chunk + decode launch takes (1,024): the
+    chunk units and the decode rows then run as two launches."""
+    shape = workloads.Shape("many", "bf16", 32, 8, 128, 16)
+    n_chunk, n_dec = 12, 1088
+    lens = [300 + 25 * i for i in range(n_chunk)] + [20 + (7 * i) % 100 for i in range(n_dec)]
+    qls = [40 + 5 * i for i in range(n_chunk)] + [1] * n_dec
+    wl = workloads.make_workload(2, seed=93, device="cuda", seq_lens=lens, q_lens=qls, shape=shape)
+    log(f"[many] {len(lens)} sequences, {n_chunk} chunks")
+    out, err = run_and_compare(wl, force_chunked=True)
+    log(f"[many] max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 EDGE = [
     # dtype, Hq, Hkv, D, B, seq_lens, q_lens
     ("bf16", 32, 8, 128, 16, [1, 2, 15, 16, 17, 31, 32, 33], None),
