@@ -601,9 +601,14 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p, bool stream) {
+// The policy is a template parameter: as a run-time argument the two loads
+// of the same address get merged before inlining, which drops the
+// non-temporal hint.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  return stream ? __builtin_nontemporal_load(q) : *q;
+  if constexpr (STREAM) return __builtin_nontemporal_load(q);
+  else return *q;
 }
 
 // Fragment sets of the balanced-decode rings (steps in flight + 1); with
@@ -651,13 +656,13 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
       const int pos = c + tok_k + 4 * x;
       const uint8_t* kp = kbase + block_id(pos) * blk_stride + (int64_t)(pos & (B - 1)) * D;
 #pragma unroll
-      for (int p = 0; p < KP; ++p) f.k[x][p] = load_u32x4(kp + 16 * p, STREAM);
+      for (int p = 0; p < KP; ++p) f.k[x][p] = load_u32x4<STREAM>(kp + 16 * p);
     }
     const int pv = c + 16 * j4;
     const int bv = block_id(pv);
     const uint8_t* vp = vbase + bv * blk_stride + (pv & (B - 1));
 #pragma unroll
-    for (int n = 0; n < NT; ++n) f.v[n] = load_u32x4(vp + (int64_t)16 * n * B, STREAM);
+    for (int n = 0; n < NT; ++n) f.v[n] = load_u32x4<STREAM>(vp + (int64_t)16 * n * B);
     f.ks = a.k_scales[(int64_t)bv * Hkv + v.kvh];
     f.vs = a.v_scales[(int64_t)bv * Hkv + v.kvh];
   };
