@@ -1110,10 +1110,10 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
 // workgroups so that each XCD (workgroups are dealt to the 8 XCDs
 // round-robin) takes a contiguous run, which keeps a unit's K/V in one L2.
 //
-// One workgroup of 4 waves per CU (one wave per SIMD, up to 512 registers).
-// A wave owns 64 query rows as two halves of 32, so every K and V fragment
-// it reads from LDS feeds two MFMAs.  Per 32-key step a wave issues 16
-// MFMAs for S^T = K Q^T and 16 for O^T = V^T P^T.
+// One workgroup per CU: 8 waves (two per SIMD, up to 256 registers each)
+// for head_dim 128, 4 for head_dim 64; a wave owns 32 query rows
+// (PrefillShape).  Per 32-key step a wave issues D/16 MFMAs for
+// S^T = K Q^T and D/16 for O^T = V^T P^T.
 //
 // S^T = K Q^T (A = K rows of the step, B = Q^T): the accumulator gives lane
 // l the 16 scores of query row l%32 at MFMA rows (r/4)*8 + 4*(l/32) + r%4.
@@ -1371,10 +1371,23 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
       const int64_t trow = (int64_t)s * a.max_blocks;
       // Block ids: a window of 64 logical blocks, one per lane, read with
       // readlane.  Ids are clamped when a window becomes current, not when it
-      // is loaded: the prefetched next window is not waited for early.
+      // is loaded: the prefetched next window is not waited for early.  The
+      // current window is kept as each block's byte offset in the pool (two
+      // dwords per lane), so a load's block base is two readlanes and an add.
       auto window = [&](int b0) { return a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)]; };
+      const uint64_t blk_bytes = (uint64_t)blk_stride * 2;
+      uint32_t woff_lo, woff_hi;
+      auto set_window = [&](int id) {
+        const uint64_t off = (uint64_t)(uint32_t)clampi(id, 0, a.num_blocks - 1) * blk_bytes;
+        woff_lo = (uint32_t)off;
+        woff_hi = (uint32_t)(off >> 32);
+      };
+      auto block_off = [&](int idx) {
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(woff_hi, idx) << 32) |
+               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(woff_lo, idx);
+      };
       int blk0 = k_begin >> lg;
-      int wid = clampi(window(blk0), 0, a.num_blocks - 1);
+      set_window(window(blk0));
       int wid_next = window(blk0 + 64);
       const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * B * D;
       const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D * B;
@@ -1384,7 +1397,7 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
       auto dma = [&](int c, int st) {
         if ((c >> lg) - blk0 >= 64) {  // wave-uniform: next window of block ids
           blk0 += 64;
-          wid = clampi(wid_next, 0, a.num_blocks - 1);
+          set_window(wid_next);
           wid_next = window(blk0 + 64);
         }
         const int cb = (c >> lg) - blk0;
@@ -1394,14 +1407,13 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
         for (int x2 = 0; x2 < IPW; ++x2) {
           const int x = w * IPW + x2;
           const int kb = (x * RPI) >> lg;  // block of these K rows inside the step
-          const int kid = __builtin_amdgcn_readlane(wid, min(cb + kb, cmax));
           const char* ksrc = reinterpret_cast<const char*>(
-              kbase + (int64_t)kid * blk_stride + (cin + ((x * RPI) & (Bs - 1))) * D);
+                                 kbase + (cin + ((x * RPI) & (Bs - 1))) * D) +
+                             block_off(min(cb + kb, cmax));
           load_to_lds(ksrc + k_voff[x2], &smem[st][0][x * 512]);
           const int vb = __builtin_amdgcn_readfirstlane(v_bi[x2]);
-          const int vid = __builtin_amdgcn_readlane(wid, min(cb + vb, cmax));
           const char* vsrc =
-              reinterpret_cast<const char*>(vbase + (int64_t)vid * blk_stride + cin);
+              reinterpret_cast<const char*>(vbase + cin) + block_off(min(cb + vb, cmax));
           load_to_lds(vsrc + v_voff[x2], &smem[st][1][x * 512]);
         }
       };
@@ -1494,8 +1506,10 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
 #pragma unroll
           for (int hf = 0; hf < H; ++hf) m[hf] = mxn[hf];
         }
-        const int i_end = min(g0 + GS, nsteps);
-        for (int i = g0; i < i_end; ++i) {
+#pragma unroll
+        for (int ii = 0; ii < GS; ++ii) {
+          const int i = g0 + ii;
+          if (i >= nsteps) break;
           const int st_next = st_cur + 1 == NS ? 0 : st_cur + 1;
           const int c = k_begin + 32 * i;
           if (grow) {
