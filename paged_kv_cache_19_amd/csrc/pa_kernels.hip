@@ -1845,6 +1845,24 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a) {
 // pairs in parallel, then own head_dim columns while summing the weighted
 // partial outputs.
 // ---------------------------------------------------------------------------
+// The sequence holding query row t (the largest s with qsl[s] <= t; qsl is
+// non-decreasing) by a 64-way search: every lane tests one candidate and a
+// ballot picks the answer, two rounds of loads for up to 4,096 sequences
+// (more rounds beyond).  All 64 lanes of the wave call it.
+__device__ __forceinline__ int seq_of_row(const int32_t* qsl, int S, int t, int lane) {
+  int lo = 0, n = S;  // the answer lies in [lo, lo + n)
+  while (n > 1) {
+    const int k = (n + 63) >> 6;  // candidates lo, lo + k, lo + 2k, ...
+    const int c = lo + lane * k;
+    const bool ok = lane * k < n && qsl[c] <= t;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+    const int last = m ? 63 - __builtin_clzll(m) : 0;  // qsl[0] = 0 <= t always holds
+    lo += last * k;
+    n = min(k, n - last * k);
+  }
+  return lo;
+}
+
 template <int ES, int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single) {
   constexpr int DD = D / 64;
@@ -1853,16 +1871,11 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single)
   const int h = blockIdx.x * 4 + wave;
   const int t = blockIdx.y;  // query token row
   if (h >= a.num_q_heads) return;
+  const int64_t orow = (int64_t)t * a.num_q_heads + h;
+  // Issued before the sequence lookup, which it does not depend on.
+  const int pieces = a.row_pieces ? a.row_pieces[orow] : 0;
   int s = t;
-  if (a.query_start_loc) {  // largest s with qsl[s] <= t
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.query_start_loc[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
-    s = lo;
-  }
+  if (a.query_start_loc) s = seq_of_row(a.query_start_loc, a.num_seqs, t, lane);
   int r0, qn;
   seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
   const int j = t - r0;
@@ -1872,8 +1885,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single)
   const int nblk = table_blocks(L, a.log2_block, a.max_blocks);
   const int kl = min(L - qn + j + 1, nblk << a.log2_block);
   if (kl <= 0) return;
-  const int64_t orow = (int64_t)t * a.num_q_heads + h;
-  const int ns = min(a.row_pieces ? a.row_pieces[orow] : (kl + a.split_tokens - 1) / a.split_tokens,
+  const int ns = min(a.row_pieces ? pieces : (kl + a.split_tokens - 1) / a.split_tokens,
                      a.max_splits);
   if (ns <= 1) return;
   const float* ml = a.part_ml + orow * a.max_splits * 2;
