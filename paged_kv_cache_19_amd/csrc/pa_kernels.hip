@@ -1216,9 +1216,12 @@ __device__ __forceinline__ void prefill_prefix(const AttnArgs& a, int* seq_prefi
 
 // The chunk units' work of workgroup wg of num_wgs (a multiple of 8), given
 // the step prefix sums.  Every wave of the workgroup takes part (barriers).
-template <int D>
+// CPB is the number of 8-key chunks one block holds inside a 32-key step
+// (min(B, 32) / 8): fixed at compile time, so the V^T tile's head_dim tiles
+// sit at constant offsets from a lane's read address.
+template <int D, int CPB>
 __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq_prefix, int wg,
-                                               int num_wgs) {
+                                               int num_wgs, uint16_t (*smem)[2][32 * D]) {
   constexpr int H = PrefillShape<D>::kHalves;    // 32-row halves per wave
   constexpr int NW = PrefillShape<D>::kWaves;
   constexpr int ROWS = PrefillShape<D>::kRows;
@@ -1231,7 +1234,7 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
   constexpr int NS = kPrefillStages;
   constexpr int GS = kPrefillGroup;
   constexpr int TILE = 32 * D;                   // elements of one K or V^T tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NS][2][TILE];
+  static_assert(TILE == 32 * D, "stage layout");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // known wave-uniform
@@ -1242,9 +1245,9 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
   const int Hkv = a.num_kv_heads;
   const int lg = a.log2_block;
   const int B = 1 << lg;
-  const int Bs = min(B, 32);     // keys of one block inside a step
-  const int cpb = Bs >> 3;       // 8-key chunks of one block inside a step (1, 2, 4)
-  const int lcpb = cpb == 4 ? 2 : cpb - 1;
+  constexpr int Bs = 8 * CPB;    // keys of one block inside a step
+  constexpr int cpb = CPB;       // 8-key chunks of one block inside a step (1, 2, 4)
+  constexpr int lcpb = cpb == 4 ? 2 : cpb - 1;
 
   const int N = seq_prefix[S];
   if (N == 0) return;
@@ -1636,13 +1639,25 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
 }
 
 
+// prefill_ranges for the block size of the call (B >= 8 on this path).
+template <int D>
+__device__ __forceinline__ void prefill_ranges_any(const AttnArgs& a, const int* seq_prefix,
+                                                   int wg, int num_wgs) {
+  // The ring of K / V^T stages (one per workgroup, whatever the block size).
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kPrefillStages][2][32 * D];
+  const int cpb = min(1 << a.log2_block, 32) >> 3;
+  if (cpb == 1) prefill_ranges<D, 1>(a, seq_prefix, wg, num_wgs, smem);
+  else if (cpb == 2) prefill_ranges<D, 2>(a, seq_prefix, wg, num_wgs, smem);
+  else prefill_ranges<D, 4>(a, seq_prefix, wg, num_wgs, smem);
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
     amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
 void prefill_kernel(AttnArgs a, int num_wgs) {
   extern __shared__ int seq_prefix[];  // [num_seqs + 1] steps
   prefill_prefix<D>(a, seq_prefix);
-  prefill_ranges<D>(a, seq_prefix, blockIdx.x, num_wgs);
+  prefill_ranges_any<D>(a, seq_prefix, blockIdx.x, num_wgs);
 }
 
 // Chunk units and single-token rows of one call in one persistent launch:
@@ -1698,7 +1713,7 @@ void chunk_mix_kernel(AttnArgs a, int num_wgs, StreamKHeader* hdr) {
       hdr->total_steps = 0;
       hdr->waves = 0;
     }
-    prefill_ranges<D>(a, seq_prefix, blockIdx.x, w_pf);
+    prefill_ranges_any<D>(a, seq_prefix, blockIdx.x, w_pf);
     return;
   }
   const int64_t waves = (int64_t)w_dec * NW;
