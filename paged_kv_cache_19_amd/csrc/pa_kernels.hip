@@ -1671,12 +1671,15 @@ void prefill_kernel(AttnArgs a, int num_wgs) {
 // workgroups run prefill_ranges; each wave of a decode workgroup is one wave
 // of the balanced decode (two fragment sets, so that both kinds fit the same
 // 256-register budget).
-// Relative CU-time per step (D = 128; half at D = 64).  A chunk step
-// (256 rows x 32 keys) takes ~1.49 us of a CU; the decode cost is the value
-// at which the chunked-prefill mix (4 x 512-token chunks + 60 decode rows)
-// ran fastest over a sweep of 410..2000 (it is worth more than its bytes at
-// the HBM rate: a CU streams far below its share of HBM bandwidth).
-constexpr int64_t kChunkStepNs = 1490;
+// Relative CU-time per step (D = 128; half at D = 64), in ns of one CU.
+// Both are the values at which the chunked-prefill mix (4 x 512-token chunks
+// + 60 decode rows) ran fastest in steady state (after the clocks have
+// ramped up): decode swept over 410..2000 with the chunk cost at 1490, then
+// the chunk cost over 1100..2400 (64 of 256 workgroups on the decode rows;
+// 56 and 72 were 10% and 3.5% slower).  The decode step is worth more than
+// its bytes at the HBM rate: a CU streams far below its share of HBM
+// bandwidth.
+constexpr int64_t kChunkStepNs = 1750;
 constexpr int64_t kDecodeStepNs = 700;
 
 template <int D>
