@@ -53,6 +53,23 @@ def test_chunk_ranges_agree(split):
     assert err <= TOL["bf16"]
 
 
+def test_merge_finds_sequences_among_thousands():
+    """The merge finds each row's sequence by a 64-way search over the query
+    offsets: with 5,000 sequences it takes three rounds (beyond 4,096), and
+    fixed 64-key splits send every row through it (fp32, vector-ALU path)."""
+    import random
+    rng = random.Random(95)
+    n = 5000
+    lens = [rng.randint(65, 200) for _ in range(n)]
+    qls = [rng.choice([1, 1, 1, 2, 3]) for _ in range(n)]
+    shape = workloads.Shape("many-seqs", "f32", 8, 2, 64, 4)
+    wl = workloads.make_workload(2, seed=95, device="cuda", seq_lens=lens, q_lens=qls, shape=shape)
+    log(f"[merge search] {n} sequences, {sum(qls)} query rows")
+    out, err = run_and_compare(wl, kv_split_tokens=64, force_chunked=True, max_seqs=300)
+    log(f"[merge search] max abs err {err:.3e}")
+    assert err <= TOL["f32"]
+
+
 def test_chunks_beyond_one_launch():
     """More sequences than the fused chunk + decode launch takes (1,024): the
     chunk units and the decode rows then run as two launches."""
