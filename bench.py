@@ -93,6 +93,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget for the oracle baseline")
+    p.add_argument("--flush", action="store_true",
+                   help="write a 1 GiB scratch buffer before every step, outside the timed "
+                        "events, so that no step reads K/V left in the 256 MB Infinity Cache "
+                        "by the step before; ms_per_step is then the mean of per-step events")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="also run one plain device copy of BYTES bytes (a reference for "
                         "hardware byte counters)")
@@ -244,7 +248,13 @@ def main():
                            wl.scale, kv_split_tokens=args.kv_split, block_refcounts=refcounts,
                            out=out, workspace=ws)
 
-    def step(ev=None):
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+
+    def step(ev=None, sev=None):
+        if scratch is not None:
+            scratch.fill_(1)  # evicts the Infinity Cache; outside every timed event
+        if sev is not None:
+            sev[0].record(stream)
         binding.compute_slot_mapping(bt, lens, qsl, shp.block_size, num_tokens=T, out=slots)
         if fp8:
             binding.reshape_and_cache_fp8(t["key"], t["value"], t["k_cache8"], t["v_cache8"],
@@ -256,6 +266,8 @@ def main():
         attention()
         if ev is not None:
             ev[1].record(stream)
+        if sev is not None:
+            sev[1].record(stream)
 
     if args.copy_probe:
         src = torch.empty(args.copy_probe, dtype=torch.uint8, device=dev)
@@ -272,14 +284,18 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)] if args.flush else [None] * args.steps
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k], sevs[k])
     stop.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    if args.flush:  # the flushes are not part of the step
+        ms_step = sum(a.elapsed_time(b) for a, b in sevs) / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = sum(attn_ms) / len(attn_ms)
     call = "pa_chunked_prefill" if chunked else ("pa_decode_fp8" if fp8 else "pa_decode")
@@ -350,6 +366,7 @@ def main():
             "kv_bytes": kv_bytes,
             "kv_split_tokens": args.kv_split,
             "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + {call}",
+            "infinity_cache_flushed": bool(args.flush),
         },
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
