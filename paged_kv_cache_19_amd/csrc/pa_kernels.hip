@@ -21,6 +21,9 @@
 //   merge_streamk_kernel         log-sum-exp merge of its pieces
 //   prefill_kernel<D>            causal query chunks on
 //                                v_mfma_f32_32x32x16_bf16, K/V staged in LDS
+//   chunk_mix_kernel<D>          the query chunks and the single-token rows
+//                                of one call in one persistent launch, the
+//                                CUs split between the two kinds of work
 //   attn_mfma_kernel<D>          fixed-split bf16 decode
 //   attn_valu_kernel<ES, D>      fp32 (and small-block bf16) split-K attention
 //                                on the vector ALUs

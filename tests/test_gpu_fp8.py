@@ -150,6 +150,25 @@ def test_fp8_relabelled_blocks_give_bit_identical_output():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
+def test_fp8_refcount_hint_changes_nothing():
+    """On the fp8 cache too the reference counts choose only the cache policy
+    (shared-prefix blocks through the caches, the rest streamed): outputs
+    with and without them are bit-identical on the shared-prefix batch."""
+    wl = workloads.make_workload(4, device="cuda", kv_fp8=True)
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    lens = wl.seq_lens_tensor("cuda")
+    rc = wl.block_refcounts_tensor("cuda")
+    assert int(rc.max()) == wl.num_seqs
+    args = (t["query"], t["k_cache8"], t["v_cache8"], t["k_scales"], t["v_scales"], bt, lens,
+            wl.max_seq_len, wl.scale)
+    a = binding.decode_fp8(*args)
+    b = binding.decode_fp8(*args, block_refcounts=rc)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a.float()).all()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_fp8_argument_errors():
     shape = workloads.Shape("fp8-args", workloads.BF16, 8, 2, 128, 8)
     wl = workloads.make_workload(2, seed=3, device="cuda", seq_lens=[20, 9], shape=shape,
