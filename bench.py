@@ -90,6 +90,9 @@ def parse():
     p.add_argument("--workload", type=int, default=3, choices=sorted(SEQ_LENS))
     p.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"])
     p.add_argument("--kv-split", type=int, default=0, help="keys per split (0: library default)")
+    p.add_argument("--shared-prefix", action="store_true",
+                   help="decode through pa_decode_shared_prefix, which reads the blocks every "
+                        "table starts with once per group of sequences (workload 4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget for the oracle baseline")
@@ -203,6 +206,11 @@ def main():
               "split)", file=sys.stderr)
         sys.exit(2)
 
+    if args.shared_prefix and (args.workload == 5 or args.kv_split):
+        print("--shared-prefix is a decode of the balanced kind (no chunked prefill, no fixed "
+              "split)", file=sys.stderr)
+        sys.exit(2)
+
     import torch
 
     from paged_kv_cache_19_amd import binding, workloads
@@ -220,7 +228,14 @@ def main():
     qsl = wl.query_start_loc_tensor(dev) if chunked else None
     T, Hq, D = t["query"].shape
     S = wl.num_seqs
-    if chunked:
+    prefix_blocks = len(wl.shared_blocks)
+    if args.shared_prefix and prefix_blocks == 0:
+        print("--shared-prefix: this workload's tables share no prefix", file=sys.stderr)
+        sys.exit(2)
+    if args.shared_prefix:
+        ws_bytes = binding.decode_shared_prefix_workspace_bytes(S, Hq, D, wl.max_seq_len,
+                                                                shp.block_size, prefix_blocks)
+    elif chunked:
         ws_bytes = binding.chunked_prefill_workspace_bytes(S, T, Hq, D, wl.max_seq_len,
                                                            shp.block_size, args.kv_split)
     elif fp8:
@@ -234,7 +249,13 @@ def main():
     stream = torch.cuda.current_stream()
 
     def attention():
-        if chunked:
+        if args.shared_prefix:
+            kc, vc = (t["k_cache8"], t["v_cache8"]) if fp8 else (t["k_cache"], t["v_cache"])
+            scales = dict(k_scales=t["k_scales"], v_scales=t["v_scales"]) if fp8 else {}
+            binding.decode_shared_prefix(t["query"], kc, vc, bt, lens, wl.max_seq_len, wl.scale,
+                                         prefix_blocks, block_refcounts=refcounts, out=out,
+                                         workspace=ws, **scales)
+        elif chunked:
             binding.chunked_prefill(t["query"], t["k_cache"], t["v_cache"], bt, lens, qsl,
                                     wl.max_seq_len, wl.max_query_len, wl.scale,
                                     kv_split_tokens=args.kv_split, block_refcounts=refcounts,
@@ -299,6 +320,8 @@ def main():
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = sum(attn_ms) / len(attn_ms)
     call = "pa_chunked_prefill" if chunked else ("pa_decode_fp8" if fp8 else "pa_decode")
+    if args.shared_prefix:
+        call = "pa_decode_shared_prefix"
     print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, {call} avg "
           f"{attn_avg:.4f} ms (p10 {percentile(attn_ms, 10):.4f}, median "
           f"{percentile(attn_ms, 50):.4f}, p90 {percentile(attn_ms, 90):.4f})",
@@ -333,7 +356,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "bytes_per_launch": call_bytes,
             "avg_launch_ms": round(attn_avg, 5),
-            "traffic": measured_traffic(args.workload, args.kv_dtype),
+            "traffic": None if args.shared_prefix else measured_traffic(args.workload,
+                                                                        args.kv_dtype),
         }
     roofline["p10_ms"] = round(percentile(attn_ms, 10), 5)
     roofline["median_ms"] = round(percentile(attn_ms, 50), 5)
@@ -366,6 +390,7 @@ def main():
             "kv_bytes": kv_bytes,
             "kv_split_tokens": args.kv_split,
             "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + {call}",
+            "shared_prefix_blocks": prefix_blocks if args.shared_prefix else 0,
             "infinity_cache_flushed": bool(args.flush),
         },
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),

@@ -299,6 +299,48 @@ int pa_decode_fp8(void* out, const void* query, const void* k_cache,
                   int32_t num_blocks, float scale, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Workspace for pa_decode_shared_prefix; 0 for invalid arguments (also
+ * when prefix_blocks * block_size > max_seq_len). */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t max_seq_len,
+                                               int32_t block_size, int32_t prefix_blocks);
+
+/*
+ * pa_decode_shared_prefix -- pa_decode (k_scales = v_scales = NULL: bf16
+ * pools) or pa_decode_fp8 (both scale arrays given: e4m3 pools) for a batch
+ * whose block tables all begin with the same prefix_blocks physical blocks,
+ * the prefix sharing of "Inside vLLM ...", section "Zero-Copy Branching and
+ * Parallel Sampling" (prefix caching) and of "03 -- PagedAttention & the
+ * vLLM V1 Architecture", section "The insight: KV cache is virtual memory"
+ * (pages shared between sequences).  The result is the attention pa_decode defines; only the
+ * order of the work differs: the prefix keys of each KV head are read once
+ * per group of floor(16 / G) sequences (G = num_q_heads / num_kv_heads;
+ * the group's query rows share one matrix tile) instead of once per
+ * sequence, and each row's prefix part and own part are combined exactly
+ * (log-sum-exp) in the merge pass.  Only whole 32-key steps (64 for e4m3)
+ * of the prefix are read this way; the rest of its blocks are read with
+ * each sequence.
+ *
+ * Contract: block_tables[s][b] == block_tables[0][b] for b < prefix_blocks
+ * and seq_lens[s] >= prefix_blocks * block_size for every s (checked, with
+ * PA_ERR_INDEX, under PA_CHECK=1; otherwise results for a batch that breaks
+ * it are undefined, but every access stays in bounds).  query and out: bf16
+ * [num_seqs, num_q_heads, head_dim].  block_size >= 8 (>= 16 for e4m3);
+ * num_seqs + ceil(num_seqs / floor(16 / G)) <= 4096, else
+ * PA_ERR_UNSUPPORTED.  prefix_blocks == 0 runs pa_decode's balanced path.
+ * Other arguments, errors and the workspace ownership as for pa_decode and
+ * pa_decode_fp8.
+ */
+int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
+                            const void* v_cache, const float* k_scales,
+                            const float* v_scales, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                            const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t max_seq_len, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t prefix_blocks, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

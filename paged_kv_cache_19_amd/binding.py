@@ -54,6 +54,10 @@ SIGNATURES = {
     "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               _f32, _vp, _sz, _vp]),
 }
 
 
@@ -299,6 +303,51 @@ def decode_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
         max_seq_len, Hq, Hkv, D, B, NB, scale, _ptr(workspace), workspace.numel(),
         _stream(stream)))
+    return out
+
+
+def decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                         block_size, prefix_blocks) -> int:
+    n = lib().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                      max_seq_len, block_size, prefix_blocks)
+    if n == 0:
+        raise PAError("pa_decode_shared_prefix_workspace_bytes", -2)
+    return n
+
+
+def decode_shared_prefix(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                         scale: float, prefix_blocks: int,
+                         k_scales: Optional[torch.Tensor] = None,
+                         v_scales: Optional[torch.Tensor] = None,
+                         block_refcounts: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode (bf16 pools) or pa_decode_fp8 (e4m3 pools, with k_scales and
+    v_scales) for a batch whose tables all start with the same prefix_blocks
+    blocks."""
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = k_cache.shape
+    if query.dtype != torch.bfloat16:
+        raise ValueError("the shared-prefix decode takes a bf16 query")
+    if (k_scales is None) != (v_scales is None):
+        raise ValueError("pass both k_scales and v_scales (e4m3 pools) or neither")
+    if k_scales is not None:
+        _fp8_pool(k_cache)
+        _fp8_pool(v_cache)
+        _f32(k_scales)
+        _f32(v_scales)
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(decode_shared_prefix_workspace_bytes(S, Hq, D, max_seq_len, B,
+                                                                     prefix_blocks),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_decode_shared_prefix", lib().pa_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
+        max_seq_len, Hq, Hkv, D, B, NB, prefix_blocks, scale, _ptr(workspace),
+        workspace.numel(), _stream(stream)))
     return out
 
 

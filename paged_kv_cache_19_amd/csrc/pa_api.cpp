@@ -72,8 +72,19 @@ struct WorkspacePlan {
 // sequence and head) | header (step total, wave count, per-sequence step
 // prefix sums).  pa_decode's two paths share one region (rows = sequences),
 // so its size is the larger of the two slot counts.
+// Partial slots a row's shared-prefix entry can need: its prefix_keys
+// (<= max_seq_len) cut like any other item of the balanced decode.
+int prefix_piece_slots(int prefix_keys) {
+  const int steps = (prefix_keys + 31) / 32;
+  return (steps + pa::kPieceCostSteps + pa::kMinStepsPerWave - 1) / pa::kMinStepsPerWave + 1;
+}
+
+// With prefix_keys > 0 (pa_decode_shared_prefix) every row also holds its
+// prefix entry's pieces and the header the prefix entries' sums (at most one
+// entry per sequence).
 bool plan_workspace(int num_tokens, int num_seqs, int num_q_heads, int head_dim, int max_seq_len,
-                    int block_size, int kv_split_tokens, bool chunk_entry, WorkspacePlan* p) {
+                    int block_size, int kv_split_tokens, bool chunk_entry, WorkspacePlan* p,
+                    int prefix_keys = 0) {
   if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 ||
       max_seq_len <= 0 || !is_pow2(block_size) || block_size > 64)
     return false;
@@ -102,12 +113,14 @@ bool plan_workspace(int num_tokens, int num_seqs, int num_q_heads, int head_dim,
     p->b_ml = align_up(rb * mlb);
   } else {
     if (kv_split_tokens != 0) p->max_pieces = 0;
+    if (prefix_keys > 0) p->max_pieces += prefix_piece_slots(prefix_keys);
     const int slots = p->max_splits > p->max_pieces ? p->max_splits : p->max_pieces;
     const size_t r = (size_t)num_seqs * num_q_heads * slots;
     p->a_o = align_up(r * ob);
     p->a_ml = align_up(r * mlb);
   }
-  p->header = align_up(16 + (size_t)(num_seqs + 1) * 4);
+  const size_t entries = (size_t)num_seqs * (prefix_keys > 0 ? 2 : 1);
+  p->header = align_up(16 + (entries + 1) * 4);
   p->total = p->a_o + p->a_ml + p->rp + p->b_o + p->b_ml + p->header;
   return true;
 }
@@ -185,6 +198,25 @@ int validate_scales(const float* d_ks, const float* d_vs, int num_blocks, int nu
   return PA_OK;
 }
 
+// PA_CHECK for a shared prefix: every table starts with row 0's first
+// prefix_blocks entries and every sequence holds at least the prefix.
+int validate_prefix(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, int num_seqs,
+                    int prefix_blocks, int block_size, hipStream_t st) {
+  if (prefix_blocks > max_blocks) return PA_ERR_INDEX;
+  std::vector<int32_t> bt((size_t)num_seqs * max_blocks), lens(num_seqs);
+  if (hipMemcpyAsync(bt.data(), d_bt, bt.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(lens.data(), d_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  for (int s = 0; s < num_seqs; ++s) {
+    if ((int64_t)lens[s] < (int64_t)prefix_blocks * block_size) return PA_ERR_INDEX;
+    for (int b = 0; b < prefix_blocks; ++b)
+      if (bt[(size_t)s * max_blocks + b] != bt[b]) return PA_ERR_INDEX;
+  }
+  return PA_OK;
+}
+
 // Blocks the tables of a (validated) batch hold.
 int table_blocks_used(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, int num_seqs,
                       int block_size, hipStream_t st, std::vector<int64_t>* out) {
@@ -215,7 +247,7 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
                      int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int block_size, int num_blocks, float scale, int dtype, int kv_split_tokens,
                      void* workspace, size_t workspace_bytes, void* stream,
-                     const Fp8Kv& f8 = Fp8Kv()) {
+                     const Fp8Kv& f8 = Fp8Kv(), int prefix_blocks = 0) {
   int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
   if (num_seqs < 0 || num_tokens < 0 || max_blocks <= 0 || num_blocks <= 0 ||
@@ -227,8 +259,13 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   if ((int64_t)num_seqs * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   WorkspacePlan plan;
   const bool chunk_entry = qsl != nullptr;
+  // Shared prefix: the whole key steps (32 keys, 64 for fp8) of the first
+  // prefix_blocks blocks; the rest of them are read with each sequence.
+  const int pstep = f8.kv_fp8 ? 64 : 32;
+  const int prefix_keys =
+      prefix_blocks > 0 ? (int)((int64_t)prefix_blocks * block_size / pstep * pstep) : 0;
   if (!plan_workspace(num_tokens, num_seqs, num_q_heads, head_dim, max_seq_len, block_size,
-                      kv_split_tokens, chunk_entry, &plan))
+                      kv_split_tokens, chunk_entry, &plan, prefix_keys))
     return PA_ERR_SHAPE;
   if (plan.max_splits > 65535) return PA_ERR_UNSUPPORTED;
   if (!workspace) return PA_ERR_WORKSPACE;
@@ -248,6 +285,11 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     rc = validate_metadata(block_tables, max_blocks, seq_lens, qsl, num_seqs, num_tokens,
                            max_seq_len, max_query_len, block_size, num_blocks, st);
     if (rc != PA_OK) return rc;
+    if (prefix_blocks > 0) {
+      rc = validate_prefix(block_tables, max_blocks, seq_lens, num_seqs, prefix_blocks,
+                           block_size, st);
+      if (rc != PA_OK) return rc;
+    }
     if (f8.kv_fp8) {
       std::vector<int64_t> used;
       rc = table_blocks_used(block_tables, max_blocks, seq_lens, num_seqs, block_size, st, &used);
@@ -298,6 +340,11 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     a.sk_part_o = a.part_o;   // pa_decode: one region, rows = sequences
     a.sk_part_ml = a.part_ml;
     a.sk_slots = plan.max_pieces;
+    if (prefix_keys > 0) {
+      a.prefix_keys = prefix_keys;
+      a.prefix_group = 16 / G;  // sequences whose G query rows fill one 16-row tile
+      a.prefix_slots = prefix_piece_slots(prefix_keys);
+    }
     err = pa::launch_decode_streamk(a, header, st);
   } else {
     if (a.kv_fp8) return PA_ERR_UNSUPPORTED;  // the fp8 cache has the balanced decode only
@@ -554,6 +601,49 @@ size_t pa_decode_fp8_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
                                      int32_t max_seq_len, int32_t block_size) {
   if (block_size < 16) return 0;
   return pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, block_size, 0);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t head_dim, int32_t max_seq_len,
+                                               int32_t block_size, int32_t prefix_blocks) {
+  if (prefix_blocks < 0 || block_size < 8) return 0;
+  WorkspacePlan p;
+  if ((int64_t)prefix_blocks * block_size > max_seq_len) return 0;
+  const int64_t pk = (int64_t)prefix_blocks * block_size / 32 * 32;
+  if (!plan_workspace(num_seqs, num_seqs, num_q_heads, head_dim, max_seq_len, block_size, 0,
+                      false, &p, (int)pk))
+    return 0;
+  return p.total;
+}
+
+int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
+                            const void* v_cache, const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* block_refcounts, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t prefix_blocks, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (prefix_blocks < 0 || (k_scales == nullptr) != (v_scales == nullptr)) return PA_ERR_SHAPE;
+  const bool fp8 = k_scales != nullptr;
+  if (block_size > 0 && block_size < (fp8 ? 16 : 8)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)prefix_blocks * block_size > max_seq_len ||
+      prefix_blocks > max_blocks_per_seq)
+    return PA_ERR_SHAPE;
+  if (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+      num_q_heads / num_kv_heads <= 16) {
+    const int spg = 16 / (num_q_heads / num_kv_heads);
+    if ((int64_t)num_seqs + (num_seqs + spg - 1) / spg > kMaxBalancedSeqs)
+      return PA_ERR_UNSUPPORTED;
+  }
+  Fp8Kv f8;
+  f8.kv_fp8 = fp8 ? 1 : 0;
+  f8.k_scales = k_scales;
+  f8.v_scales = v_scales;
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                          PA_BF16, 0, workspace, workspace_bytes, stream, f8, prefix_blocks);
 }
 
 int pa_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -35,7 +35,21 @@ struct AttnArgs {
   int32_t kv_fp8;           // 1: e4m3 cache with per-(block, KV head) scales, bf16 q/out
   const float* k_scales;    // [NB, Hkv] (kv_fp8 only)
   const float* v_scales;    // [NB, Hkv]
+  // Shared-prefix decode (balanced decode only; 0: off).  Keys [0,
+  // prefix_keys) of every sequence are the blocks table row 0 starts with;
+  // they are read once per group of prefix_group sequences (one 16-row MFMA
+  // tile of query rows), and each sequence's own items cover the keys after
+  // them.  Every row is then left as pieces: the prefix pieces in the last
+  // prefix_slots of its sk_slots.
+  int32_t prefix_keys;
+  int32_t prefix_group;
+  int32_t prefix_slots;
 };
+
+// Work-list entries for the prefixes: one per group of sequences.
+__host__ __device__ inline int prefix_items(int num_seqs, int group) {
+  return group > 0 ? (num_seqs + group - 1) / group : 0;
+}
 
 // Balanced decode: every resident wave streams at least this many 32-key
 // steps, which bounds the pieces one row can be cut into.

@@ -913,20 +913,32 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t g, int64_t waves, int64_
 // Decode steps (per KV head) of every sequence's single-token rows in
 // P[s + 1] and the lengths in Ls[s], by nthreads threads; the caller
 // synchronises before the scan.
+//
+// Shared-prefix decode (a.prefix_keys > 0): entries S .. S + ng - 1 are the
+// prefix items, one per group of a.prefix_group sequences, and a sequence's
+// own item covers its keys after the prefix.
 template <bool FP8>
 __device__ __forceinline__ void decode_prefix_fill(const AttnArgs& a, int* P, int* Ls, int tid,
                                                    int nthreads) {
   constexpr int STEP = FP8 ? 64 : 32;
   constexpr int LSTEP = FP8 ? 6 : 5;
   const int lg = a.log2_block;
-  for (int s = tid; s < a.num_seqs; s += nthreads) {
+  const int S = a.num_seqs;
+  const int pk = a.prefix_keys;  // a multiple of STEP (checked by the host)
+  const int ng = prefix_items(S, a.prefix_group);
+  for (int s = tid; s < S + ng; s += nthreads) {
+    if (s >= S) {  // a prefix item
+      P[s + 1] = (pk >> LSTEP) + kPieceCostSteps;
+      Ls[s] = pk;
+      continue;
+    }
     const int L = a.seq_lens[s];
     int r0, qn;
     seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
     const int kl = min(L, table_blocks(L, lg, a.max_blocks) << lg);
     // Only single-token rows are decode work (query chunks have their own kernel).
     // An item's cost is its steps plus kPieceCostSteps for starting a piece.
-    P[s + 1] = (qn == 1 && kl > 0) ? ((kl + STEP - 1) >> LSTEP) + kPieceCostSteps : 0;
+    P[s + 1] = (qn == 1 && kl > pk) ? ((kl - pk + STEP - 1) >> LSTEP) + kPieceCostSteps : 0;
     Ls[s] = L;
   }
 }
@@ -958,7 +970,7 @@ template <int D, bool FP8, int NSETS>
 __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, const int* Ls,
                                              int64_t N, int64_t weff, int w) {
   constexpr int STEP = FP8 ? 64 : 32;
-  const int S = a.num_seqs;
+  const int S = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);  // work-list entries
   const int Hkv = a.num_kv_heads;
   int64_t g = (int64_t)w * N / weff;
   const int64_t g_end = (int64_t)(w + 1) * N / weff;
@@ -986,16 +998,36 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     if (c1 <= c0) continue;  // the share holds only the start-up cost of this item
     const int64_t wf = wave_of_step(g_item, weff, N);
     const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
-    int r0, qn;
-    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-    const SeqView v = seq_view(a, s, kvh, Ls[s], r0, 1);
+    const bool pfx = s >= a.num_seqs;  // a shared-prefix item
+    SeqView v;
+    if (pfx) {
+      // The prefix blocks through table row 0, for the query rows of a
+      // group of sequences: chunk token j of this view is sequence r0 + j,
+      // and every row sees all prefix keys.
+      const int k = s - a.num_seqs;
+      const int qg = min(a.prefix_group, a.num_seqs - a.prefix_group * k);
+      v.s = 0;
+      v.kvh = kvh;
+      v.L = a.prefix_keys + qg;
+      v.r0 = a.prefix_group * k;
+      v.qn = qg;
+      v.nblk = a.prefix_keys >> a.log2_block;
+      v.kcap = a.prefix_keys;
+    } else {
+      int r0, qn;
+      seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+      v = seq_view(a, s, kvh, Ls[s], r0, 1);
+    }
     const int kl = min(v.L, v.kcap);
     RowState<D, 1> st;
     load_rows<D, 1, FP8>(a, v, 0, st);
-    const int k_begin = c0 * STEP;
-    const int k_end = min(c1 * STEP, kl);
-    const int k_sh =
-        k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) & ~(STEP - 1) : 0;
+    const int kb0 = pfx ? 0 : a.prefix_keys;  // the item's step 0 starts at this key
+    const int k_begin = kb0 + c0 * STEP;
+    const int k_end = min(kb0 + c1 * STEP, kl);
+    const int k_sh = pfx ? kl  // the prefix is shared by construction
+                         : k_begin < (64 << a.log2_block)
+                               ? leading_shared_keys(a, v) & ~(STEP - 1)
+                               : 0;
     if constexpr (FP8) {
       if (k_sh > k_begin) attend_fp8<D, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
       if (k_end > max(k_begin, k_sh))
@@ -1006,8 +1038,18 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
       if (k_end > max(k_begin, k_sh))
         attend<D, 1, true, NSETS>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     }
-    write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
-                     PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
+    if (a.prefix_keys > 0) {  // every row is merged with its other part: pieces only
+      // own pieces in slots [0, own), prefix pieces in [own, sk_slots); a
+      // piece past its range (out-of-contract lengths) is dropped
+      const int own = a.sk_slots - a.prefix_slots;
+      const int piece = (int)(w - wf);
+      const int slot = pfx ? own + piece : (piece < own ? piece : a.sk_slots);
+      write_rows<D, 1>(a, v, 0, st, false, slot,
+                       PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, -1});
+    }
+    else
+      write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
+                       PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
   }
 }
 
@@ -1017,8 +1059,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2, (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2)))
 void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
   extern __shared__ int smem[];
-  const int S = a.num_seqs;
-  int* P = smem;           // [S + 1] steps before sequence s (per KV head)
+  const int S = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);  // work-list entries
+  int* P = smem;           // [S + 1] steps before entry s (per KV head)
   int* Ls = smem + S + 1;  // [S]     sequence lengths
   const int lane = threadIdx.x;
   const int w = blockIdx.x;
@@ -1040,8 +1082,22 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
   decode_share<D, FP8, kDecodeSets>(a, P, Ls, N, weff, w);
 }
 
+// Pieces of work-list entry e for KV head kvh: the waves whose shares
+// intersect the entry's step range (0 when the entry has no steps).
+__device__ __forceinline__ int entry_pieces(const int* P, int e, int Hkv, int kvh, int64_t weff,
+                                            int64_t N) {
+  const int cost = P[e + 1] - P[e];
+  if (cost <= 0) return 0;
+  const int64_t g_item = (int64_t)Hkv * P[e] + (int64_t)kvh * cost + kPieceCostSteps;
+  const int64_t wf = wave_of_step(g_item, weff, N);
+  const int64_t wl = wave_of_step(g_item + (cost - kPieceCostSteps) - 1, weff, N);
+  return (int)(wl - wf + 1);
+}
+
 // Merge for the balanced decode: the pieces of row (s, h) are the waves whose
-// shares intersect the row's step range.
+// shares intersect the row's step range.  With a shared prefix the row also
+// has the pieces of its group's prefix entry, in the last prefix_slots slots,
+// and is always merged (its decode wrote no final row).
 template <int ES, int D>
 __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const StreamKHeader* hdr) {
   constexpr int DD = D / 64;
@@ -1054,25 +1110,27 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   const int64_t weff = hdr->waves;
   if (N <= 0 || weff <= 0) return;
   const int* P = reinterpret_cast<const int*>(hdr + 1);
-  const int cost = P[s + 1] - P[s];
-  if (cost <= 0) return;
-  const int nch = cost - kPieceCostSteps;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int kvh = h / G;
-  const int64_t g_item =
-      (int64_t)a.num_kv_heads * P[s] + (int64_t)kvh * cost + kPieceCostSteps;
-  const int64_t wf = wave_of_step(g_item, weff, N);
-  const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
-  const int ns = (int)min(wl - wf + 1, (int64_t)a.sk_slots);
-  if (ns <= 1) return;
+  const bool pfx = a.prefix_keys > 0;
+  const int own_slots = a.sk_slots - (pfx ? a.prefix_slots : 0);
+  const int n_own = min(entry_pieces(P, s, a.num_kv_heads, kvh, weff, N), own_slots);
+  const int n_pfx =
+      pfx ? min(entry_pieces(P, a.num_seqs + s / a.prefix_group, a.num_kv_heads, kvh, weff, N),
+                a.prefix_slots)
+          : 0;
+  const int ns = n_own + n_pfx;
+  if (pfx ? ns == 0 : ns <= 1) return;
   int r0, qn;
   seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-  const int64_t prow = (int64_t)s * a.num_q_heads + h;
   const int64_t orow = (int64_t)r0 * a.num_q_heads + h;
+  const int64_t prow = pfx ? orow : (int64_t)s * a.num_q_heads + h;
   const float* ml = a.sk_part_ml + prow * a.sk_slots * 2;
   const float* po = a.sk_part_o + prow * a.sk_slots * D;
+  // piece b -> its slot: the row's own pieces first, then the prefix's
+  auto slot = [&](int b) { return b < n_own ? b : own_slots + (b - n_own); };
   float M = neg_inf();
-  for (int b = lane; b < ns; b += 64) M = fmaxf(M, ml[2 * b]);
+  for (int b = lane; b < ns; b += 64) M = fmaxf(M, ml[2 * slot(b)]);
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
   float acc[DD];
@@ -1081,12 +1139,12 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   float den = 0.f;
   for (int b0 = 0; b0 < ns; b0 += 64) {
     const int b = b0 + lane;
-    const float w = b < ns ? fast_exp2(ml[2 * b] - M) : 0.f;
-    den += b < ns ? w * ml[2 * b + 1] : 0.f;
+    const float w = b < ns ? fast_exp2(ml[2 * slot(b)] - M) : 0.f;
+    den += b < ns ? w * ml[2 * slot(b) + 1] : 0.f;
     const int nb = min(64, ns - b0);
     for (int k = 0; k < nb; ++k) {
       const float wk = __shfl(w, k);
-      const float* p = po + (int64_t)(b0 + k) * D + lane;
+      const float* p = po + (int64_t)slot(b0 + k) * D + lane;
 #pragma unroll
       for (int dd = 0; dd < DD; ++dd) acc[dd] += wk * p[64 * dd];
     }
@@ -1968,9 +2026,10 @@ hipError_t resident(Residency& c, K kernel, int threads, size_t lds, int seqs, i
 template <int D, bool FP8 = false>
 hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
   static thread_local Residency cache;
-  const size_t lds = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+  const int entries = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);
+  const size_t lds = (size_t)(2 * entries + 1) * sizeof(int);
   int waves = 0;
-  hipError_t err = resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, a.num_seqs, waves);
+  hipError_t err = resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, entries, waves);
   if (err != hipSuccess) return err;
   StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
   decode_streamk_kernel<D, FP8><<<waves, 64, lds, st>>>(a, waves, hdr);

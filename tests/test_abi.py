@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding.SIGNATURES)
@@ -76,6 +76,16 @@ def test_workspace_queries(lib):
         al(2108 * 32 * 10 * 128 * 4) + al(2108 * 32 * 10 * 8) + al(2108 * 32 * 4) + \
         al(64 * 32 * 36 * 128 * 4) + al(64 * 32 * 36 * 8) + 512
     assert lib.pa_chunked_prefill_workspace_bytes(64, 2108, 32, 128, 8704, 16, 96) == 0
+    # shared prefix of 32 blocks (512 keys, 16 steps): a row also keeps up to
+    # ceil((16 + 3) / 8) + 1 = 4 prefix pieces (34 + 4 = 38 slots), and the header
+    # room for one prefix entry per sequence: 16 + 4 * (256 + 1) bytes rounded to 256
+    sp = lib.pa_decode_shared_prefix_workspace_bytes
+    assert sp(128, 64, 128, 8192, 16, 32) == \
+        128 * 64 * 38 * 128 * 4 + 128 * 64 * 38 * 2 * 4 + 1280
+    assert sp(4, 8, 64, 64, 16, 4) > 0
+    assert sp(4, 8, 64, 64, 16, 5) == 0      # prefix longer than max_seq_len
+    assert sp(4, 8, 64, 64, 4, 1) == 0       # block_size below 8
+    assert sp(4, 8, 64, 64, 16, -1) == 0
 
 
 def _decode(lib, **kw):
@@ -125,6 +135,34 @@ def test_other_entry_points_reject_bad_arguments(lib):
     args[8] = FAKE
     args[21] = None
     assert cp(*args) == -5
+
+
+def _shared(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, bt=FAKE, maxb=4, lens=FAKE,
+             S=2, maxlen=64, Hq=8, Hkv=2, D=128, B=16, NB=8, pb=2, scale=0.1, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode_shared_prefix(a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"],
+                                       a["bt"], a["maxb"], None, a["lens"], a["S"], a["maxlen"],
+                                       a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["pb"],
+                                       a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), -1), (dict(bt=None), -1), (dict(pb=-1), -2),
+    (dict(ks=FAKE), -2),                     # one scale array without the other
+    (dict(ks=FAKE, vs=FAKE, B=8), -4),       # e4m3 pools need block_size >= 16
+    (dict(B=4), -4), (dict(pb=5), -2),       # prefix past max_seq_len
+    (dict(pb=5, maxlen=256), -2),            # prefix past the table width
+    (dict(S=4000), -4),                      # 4000 + 1000 prefix entries > 4096
+    (dict(Hq=6, Hkv=4), -2), (dict(D=96), -4), (dict(ws=None), -5), (dict(wsb=16), -5),
+])
+def test_shared_prefix_decode_rejects_bad_arguments(lib, kw, code):
+    assert _shared(lib, **kw) == code
+
+
+def test_shared_prefix_decode_empty_batch_is_a_no_op(lib):
+    assert _shared(lib, S=0, out=None) == 0
 
 
 def test_binding_refuses_host_tensors(lib):
