@@ -1025,7 +1025,7 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     const int k_begin = kb0 + c0 * STEP;
     const int k_end = min(kb0 + c1 * STEP, kl);
     const int k_sh = pfx ? kl  // the prefix is shared by construction
-                         : k_begin < (64 << a.log2_block)
+                         : a.prefix_keys > 0 ? 0 : k_begin < (64 << a.log2_block)
                                ? leading_shared_keys(a, v) & ~(STEP - 1)
                                : 0;
     if constexpr (FP8) {
