@@ -312,11 +312,13 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  * the prefix sharing of "Inside vLLM ...", section "Zero-Copy Branching and
  * Parallel Sampling" (prefix caching) and of "03 -- PagedAttention & the
  * vLLM V1 Architecture", section "The insight: KV cache is virtual memory"
- * (pages shared between sequences).  The result is the attention pa_decode defines; only the
- * order of the work differs: the prefix keys of each KV head are read once
- * per group of floor(16 / G) sequences (G = num_q_heads / num_kv_heads;
- * the group's query rows share one matrix tile) instead of once per
- * sequence, and each row's prefix part and own part are combined exactly
+ * (pages shared between sequences).  The result is the attention pa_decode
+ * defines; only the order of the work differs: the prefix keys of each KV
+ * head are read once per group of sequences instead of once per sequence
+ * (G = num_q_heads / num_kv_heads; a group is floor(32 / G) sequences on
+ * bf16 pools, whose query rows fill two 16-row matrix tiles, and floor(16 /
+ * G) on e4m3 pools, one tile), and each row's prefix part and own part are
+ * combined exactly
  * (log-sum-exp) in the merge pass.  Only whole 32-key steps (64 for e4m3)
  * of the prefix are read this way; the rest of its blocks are read with
  * each sequence.
@@ -326,7 +328,7 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  * PA_ERR_INDEX, under PA_CHECK=1; otherwise results for a batch that breaks
  * it are undefined, but every access stays in bounds).  query and out: bf16
  * [num_seqs, num_q_heads, head_dim].  block_size >= 8 (>= 16 for e4m3);
- * num_seqs + ceil(num_seqs / floor(16 / G)) <= 4096, else
+ * num_seqs + ceil(num_seqs / group) <= 4096, else
  * PA_ERR_UNSUPPORTED.  prefix_blocks == 0 runs pa_decode's balanced path.
  * Other arguments, errors and the workspace ownership as for pa_decode and
  * pa_decode_fp8.

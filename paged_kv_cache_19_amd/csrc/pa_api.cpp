@@ -342,7 +342,8 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     a.sk_slots = plan.max_pieces;
     if (prefix_keys > 0) {
       a.prefix_keys = prefix_keys;
-      a.prefix_group = 16 / G;  // sequences whose G query rows fill one 16-row tile
+      // sequences whose G query rows fill the prefix item's row tiles
+      a.prefix_group = 16 * pa::prefix_tiles(f8.kv_fp8 != 0) / G;
       a.prefix_slots = prefix_piece_slots(prefix_keys);
     }
     err = pa::launch_decode_streamk(a, header, st);
@@ -632,7 +633,7 @@ int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
     return PA_ERR_SHAPE;
   if (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
       num_q_heads / num_kv_heads <= 16) {
-    const int spg = 16 / (num_q_heads / num_kv_heads);
+    const int spg = 16 * pa::prefix_tiles(fp8) / (num_q_heads / num_kv_heads);
     if ((int64_t)num_seqs + (num_seqs + spg - 1) / spg > kMaxBalancedSeqs)
       return PA_ERR_UNSUPPORTED;
   }

@@ -46,6 +46,12 @@ struct AttnArgs {
   int32_t prefix_slots;
 };
 
+// 16-row MFMA tiles of query rows per shared-prefix item: a group holds
+// floor(16 * tiles / G) sequences, and each of the item's K/V loads serves
+// all of their rows.  The fp8 item keeps one tile (two would not fit its
+// registers next to the widened codes).
+__host__ __device__ constexpr int prefix_tiles(bool fp8) { return fp8 ? 1 : 2; }
+
 // Work-list entries for the prefixes: one per group of sequences.
 __host__ __device__ inline int prefix_items(int num_seqs, int group) {
   return group > 0 ? (num_seqs + group - 1) / group : 0;

@@ -619,10 +619,10 @@ __device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p) {
 constexpr int kDecodeSets = 3;
 constexpr int kFp8Sets = 3;
 
-template <int D, bool STREAM>
+template <int D, bool STREAM, int R = 1>
 __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, int kv_wave,
                                            int kv_min, int k_begin, int k_end,
-                                           RowState<D, 1>& st) {
+                                           RowState<D, R>& st) {
   constexpr int KK = D / 32;
   constexpr int KP = D / 64;
   constexpr int NT = D / 16;
@@ -687,64 +687,74 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
         for (int n = 0; n < NT; ++n) f.v[n][w] &= keep;
       }
     }
-    f32x4 s4[4];
+    // R row tiles share the widened K and V of the step.
+    f32x4 s4[R][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) s4[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) s4[t][x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const u32x4 w = f.k[x][kk >> 1];
         const bf16x8 kf = e4m3x8_to_bf16(w[2 * (kk & 1)], w[2 * (kk & 1) + 1]);
-        s4[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, st.qf[0][kk], s4[x], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+          s4[t][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, st.qf[t][kk], s4[t][x], 0, 0, 0);
       }
     }
     const float kscale = f.ks * sl2;
-    float sv[16];
+    bf16x8 pf[R][2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int t = 0; t < R; ++t) {
+      float sv[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[4 * x + r] = s4[x][r] * kscale;
-    if (mask) {
-      rare_branch();
-      const int lim = st.klim[0] - pv;
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sv[e] = (e < lim) ? sv[e] : neg_inf();
+        for (int r = 0; r < 4; ++r) sv[4 * x + r] = s4[t][x][r] * kscale;
+      if (mask) {
+        rare_branch();
+        const int lim = st.klim[t] - pv;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sv[e] = (e < lim) ? sv[e] : neg_inf();
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+      mx = xl_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > st.m[t] + kLazyRescaleLog2) != 0) {
+        rare_branch();
+        const float mnew = fmaxf(st.m[t], mx);
+        const float alpha = fast_exp2(st.m[t] - ((mnew == neg_inf()) ? 0.f : mnew));
+        st.l[t] *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * j4 + r);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st.o[t][n][r] *= ar[r];
+        st.m[t] = mnew;
+      }
+      const float muse = (st.m[t] == neg_inf()) ? 0.f : st.m[t];
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(sv[e] - muse);
+        ps += p;
+        pf[t][e >> 3][e & 7] = static_cast<__bf16>(p * f.vs);
+      }
+      st.l[t] += xl_sum(ps);
     }
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sv[e]);
-    mx = xl_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > st.m[0] + kLazyRescaleLog2) != 0) {
-      rare_branch();
-      const float mnew = fmaxf(st.m[0], mx);
-      const float alpha = fast_exp2(st.m[0] - ((mnew == neg_inf()) ? 0.f : mnew));
-      st.l[0] *= alpha;
-      float ar[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * j4 + r);
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.o[0][n][r] *= ar[r];
-      st.m[0] = mnew;
-    }
-    const float muse = (st.m[0] == neg_inf()) ? 0.f : st.m[0];
-    float ps = 0.f;
-    bf16x8 pf[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = fast_exp2(sv[e] - muse);
-      ps += p;
-      pf[e >> 3][e & 7] = static_cast<__bf16>(p * f.vs);
-    }
-    st.l[0] += xl_sum(ps);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const bf16x8 vf = e4m3x8_to_bf16(f.v[n][2 * h2], f.v[n][2 * h2 + 1]);
-        st.o[0][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[h2], vf, st.o[0][n], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+          st.o[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[t][h2], vf, st.o[t][n], 0, 0, 0);
       }
     }
   };
@@ -966,7 +976,11 @@ __device__ __forceinline__ void decode_prefix_scan(int* P, int S, int lane) {
 
 // Wave w's share (of weff) of the N decode steps, given the step prefix sums
 // P and lengths Ls; NSETS fragment sets in the bf16 ring.
-template <int D, bool FP8, int NSETS>
+//
+// PREFIX: the shared-prefix work list (prefix items after the sequences'
+// own items); an instantiation without it holds no prefix path, so the
+// plain decode keeps its register budget.
+template <int D, bool FP8, int NSETS, bool PREFIX = false>
 __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, const int* Ls,
                                              int64_t N, int64_t weff, int w) {
   constexpr int STEP = FP8 ? 64 : 32;
@@ -998,14 +1012,15 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     if (c1 <= c0) continue;  // the share holds only the start-up cost of this item
     const int64_t wf = wave_of_step(g_item, weff, N);
     const int64_t wl = wave_of_step(g_item + nch - 1, weff, N);
-    const bool pfx = s >= a.num_seqs;  // a shared-prefix item
-    SeqView v;
-    if (pfx) {
-      // The prefix blocks through table row 0, for the query rows of a
-      // group of sequences: chunk token j of this view is sequence r0 + j,
-      // and every row sees all prefix keys.
+    const int piece = (int)(w - wf);
+    if (PREFIX && s >= a.num_seqs) {
+      // A prefix item: the prefix blocks through table row 0, for the query
+      // rows of a group of sequences (PT 16-row tiles that share every K/V
+      // load).  Chunk token j of this view is sequence r0 + j,
+      // every row sees all prefix keys, and the loads go through the caches.
       const int k = s - a.num_seqs;
       const int qg = min(a.prefix_group, a.num_seqs - a.prefix_group * k);
+      SeqView v;
       v.s = 0;
       v.kvh = kvh;
       v.L = a.prefix_keys + qg;
@@ -1013,21 +1028,34 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
       v.qn = qg;
       v.nblk = a.prefix_keys >> a.log2_block;
       v.kcap = a.prefix_keys;
-    } else {
-      int r0, qn;
-      seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-      v = seq_view(a, s, kvh, Ls[s], r0, 1);
+      const int kl = a.prefix_keys;
+      constexpr int PT = prefix_tiles(FP8);
+      RowState<D, PT> st;
+      load_rows<D, PT, FP8>(a, v, 0, st);
+      const int k_begin = c0 * STEP;
+      const int k_end = min(c1 * STEP, kl);
+      if constexpr (FP8) attend_fp8<D, false, PT>(a, v, kl, kl, k_begin, k_end, st);
+      else attend<D, PT, false, NSETS>(a, v, kl, kl, k_begin, k_end, st);
+      // prefix pieces sit in the last prefix_slots slots of each row
+      write_rows<D, PT>(a, v, 0, st, false, a.sk_slots - a.prefix_slots + piece,
+                        PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, -1});
+      continue;
     }
+    int r0, qn;
+    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+    const SeqView v = seq_view(a, s, kvh, Ls[s], r0, 1);
     const int kl = min(v.L, v.kcap);
     RowState<D, 1> st;
     load_rows<D, 1, FP8>(a, v, 0, st);
-    const int kb0 = pfx ? 0 : a.prefix_keys;  // the item's step 0 starts at this key
+    const int kb0 = a.prefix_keys;  // step 0 of an own item starts after the shared prefix
     const int k_begin = kb0 + c0 * STEP;
     const int k_end = min(kb0 + c1 * STEP, kl);
-    const int k_sh = pfx ? kl  // the prefix is shared by construction
-                         : a.prefix_keys > 0 ? 0 : k_begin < (64 << a.log2_block)
-                               ? leading_shared_keys(a, v) & ~(STEP - 1)
-                               : 0;
+    // Keys read through the caches: with a shared prefix none (what the
+    // table shares past the prefix is less than a step), else the leading
+    // shared blocks.
+    const int k_sh = a.prefix_keys > 0 ? 0
+                     : k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) & ~(STEP - 1)
+                                                      : 0;
     if constexpr (FP8) {
       if (k_sh > k_begin) attend_fp8<D, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
       if (k_end > max(k_begin, k_sh))
@@ -1038,23 +1066,21 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
       if (k_end > max(k_begin, k_sh))
         attend<D, 1, true, NSETS>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     }
-    if (a.prefix_keys > 0) {  // every row is merged with its other part: pieces only
-      // own pieces in slots [0, own), prefix pieces in [own, sk_slots); a
-      // piece past its range (out-of-contract lengths) is dropped
+    if (a.prefix_keys > 0) {
+      // every row is merged with its prefix part: own pieces in slots
+      // [0, own); a piece past that range (out-of-contract lengths) is dropped
       const int own = a.sk_slots - a.prefix_slots;
-      const int piece = (int)(w - wf);
-      const int slot = pfx ? own + piece : (piece < own ? piece : a.sk_slots);
-      write_rows<D, 1>(a, v, 0, st, false, slot,
+      write_rows<D, 1>(a, v, 0, st, false, piece < own ? piece : a.sk_slots,
                        PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, -1});
-    }
-    else
-      write_rows<D, 1>(a, v, 0, st, wf == wl, (int)(w - wf),
+    } else {
+      write_rows<D, 1>(a, v, 0, st, wf == wl, piece,
                        PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
+    }
   }
 }
 
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool PREFIX = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2, (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2)))
 void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
@@ -1079,7 +1105,7 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
     for (int s = lane; s <= S; s += 64) hp[s] = P[s];
   }
   if (w >= weff) return;
-  decode_share<D, FP8, kDecodeSets>(a, P, Ls, N, weff, w);
+  decode_share<D, FP8, kDecodeSets, PREFIX>(a, P, Ls, N, weff, w);
 }
 
 // Pieces of work-list entry e for KV head kvh: the waves whose shares
@@ -2025,14 +2051,17 @@ hipError_t resident(Residency& c, K kernel, int threads, size_t lds, int seqs, i
 
 template <int D, bool FP8 = false>
 hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
-  static thread_local Residency cache;
+  static thread_local Residency cache, cache_p;
   const int entries = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);
   const size_t lds = (size_t)(2 * entries + 1) * sizeof(int);
   int waves = 0;
-  hipError_t err = resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, entries, waves);
+  const bool prefix = a.prefix_keys > 0;
+  hipError_t err = prefix ? resident(cache_p, decode_streamk_kernel<D, FP8, true>, 64, lds, entries, waves)
+                          : resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, entries, waves);
   if (err != hipSuccess) return err;
   StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
-  decode_streamk_kernel<D, FP8><<<waves, 64, lds, st>>>(a, waves, hdr);
+  if (prefix) decode_streamk_kernel<D, FP8, true><<<waves, 64, lds, st>>>(a, waves, hdr);
+  else decode_streamk_kernel<D, FP8><<<waves, 64, lds, st>>>(a, waves, hdr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   merge_streamk_kernel<2, D><<<dim3((a.num_q_heads + 3) / 4, a.num_seqs), 256, 0, st>>>(a, hdr);
