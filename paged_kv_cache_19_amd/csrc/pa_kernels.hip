@@ -1108,6 +1108,63 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
   decode_share<D, FP8, kDecodeSets, PREFIX>(a, P, Ls, N, weff, w);
 }
 
+// Up to kMergeBatch pieces of one row held in registers, so that all of
+// their loads are in flight together (lane b also holds piece b's (m, l)).
+constexpr int kMergeBatch = 8;
+template <int D>
+struct RowPieces {
+  float o[kMergeBatch][D / 64];
+  float m, l;
+};
+
+// Loads pieces 0 .. ns-1 (ns <= kMergeBatch) of a row; slot(b) is piece b's
+// partial slot.
+template <int D, typename SlotFn>
+__device__ __forceinline__ void load_pieces(const float* ml, const float* po, int ns, SlotFn slot,
+                                            int lane, RowPieces<D>& rp) {
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    if (k < ns) {
+      const float* p = po + (int64_t)slot(k) * D + lane;
+#pragma unroll
+      for (int dd = 0; dd < D / 64; ++dd) rp.o[k][dd] = p[64 * dd];
+    }
+  }
+  rp.m = lane < ns ? ml[2 * slot(lane)] : neg_inf();
+  rp.l = lane < ns ? ml[2 * slot(lane) + 1] : 0.f;
+}
+
+// out = sum_b 2^(m_b - M) o_b / sum_b 2^(m_b - M) l_b over the loaded pieces
+// (the same operations, in the same order, as the general loops below).
+template <int ES, int D>
+__device__ __forceinline__ void combine_pieces(const RowPieces<D>& rp, int ns, void* out,
+                                               int64_t orow, int lane) {
+  constexpr int DD = D / 64;
+  // lanes past ns may hold slots loaded ahead of time that this row does
+  // not use: they take no part in the max
+  float M = lane < ns ? rp.m : neg_inf();
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
+  const float wt = lane < ns ? fast_exp2(rp.m - M) : 0.f;
+  float den = lane < ns ? wt * rp.l : 0.f;
+  float acc[DD];
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) acc[dd] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    if (k < ns) {
+      const float wk = __shfl(wt, k);
+#pragma unroll
+      for (int dd = 0; dd < DD; ++dd) acc[dd] += wk * rp.o[k][dd];
+    }
+  }
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) den += __shfl_xor(den, w);
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) store_elem<ES>(out, orow * D + lane + 64 * dd, acc[dd] * inv);
+}
+
 // Pieces of work-list entry e for KV head kvh: the waves whose shares
 // intersect the entry's step range (0 when the entry has no steps).
 __device__ __forceinline__ int entry_pieces(const int* P, int e, int Hkv, int kvh, int64_t weff,
@@ -1132,13 +1189,13 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   const int h = blockIdx.x * 4 + wave;
   const int s = blockIdx.y;
   if (h >= a.num_q_heads) return;
+  const bool pfx = a.prefix_keys > 0;
   const int64_t N = hdr->total_steps;
   const int64_t weff = hdr->waves;
   if (N <= 0 || weff <= 0) return;
   const int* P = reinterpret_cast<const int*>(hdr + 1);
   const int G = a.num_q_heads / a.num_kv_heads;
   const int kvh = h / G;
-  const bool pfx = a.prefix_keys > 0;
   const int own_slots = a.sk_slots - (pfx ? a.prefix_slots : 0);
   const int n_own = min(entry_pieces(P, s, a.num_kv_heads, kvh, weff, N), own_slots);
   const int n_pfx =
@@ -1155,6 +1212,12 @@ __global__ __launch_bounds__(256) void merge_streamk_kernel(AttnArgs a, const St
   const float* po = a.sk_part_o + prow * a.sk_slots * D;
   // piece b -> its slot: the row's own pieces first, then the prefix's
   auto slot = [&](int b) { return b < n_own ? b : own_slots + (b - n_own); };
+  if (ns <= kMergeBatch) {  // all loads in flight together
+    RowPieces<D> rp;
+    load_pieces<D>(ml, po, ns, slot, lane, rp);
+    combine_pieces<ES, D>(rp, ns, a.out, orow, lane);
+    return;
+  }
   float M = neg_inf();
   for (int b = lane; b < ns; b += 64) M = fmaxf(M, ml[2 * slot(b)]);
 #pragma unroll
@@ -1977,8 +2040,18 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single)
   const int t = blockIdx.y;  // query token row
   if (h >= a.num_q_heads) return;
   const int64_t orow = (int64_t)t * a.num_q_heads + h;
-  // Issued before the sequence lookup, which it does not depend on.
+  const float* ml = a.part_ml + orow * a.max_splits * 2;
+  const float* po = a.part_o + orow * a.max_splits * D;
+  // With recorded piece counts the row's partials are loaded before the
+  // sequence lookup, which they do not depend on (a row that turns out not
+  // to be merged here only wasted the in-bounds loads).
   const int pieces = a.row_pieces ? a.row_pieces[orow] : 0;
+  RowPieces<D> rp;
+  if (a.row_pieces) {
+    if (pieces <= 1) return;  // whole (written by the chunk kernel) or merged elsewhere
+    if (pieces <= kMergeBatch)
+      load_pieces<D>(ml, po, min(pieces, a.max_splits), [](int b) { return b; }, lane, rp);
+  }
   int s = t;
   if (a.query_start_loc) s = seq_of_row(a.query_start_loc, a.num_seqs, t, lane);
   int r0, qn;
@@ -1993,8 +2066,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int skip_single)
   const int ns = min(a.row_pieces ? pieces : (kl + a.split_tokens - 1) / a.split_tokens,
                      a.max_splits);
   if (ns <= 1) return;
-  const float* ml = a.part_ml + orow * a.max_splits * 2;
-  const float* po = a.part_o + orow * a.max_splits * D;
+  if (ns <= kMergeBatch) {
+    if (!a.row_pieces || pieces > kMergeBatch)
+      load_pieces<D>(ml, po, ns, [](int b) { return b; }, lane, rp);
+    combine_pieces<ES, D>(rp, ns, a.out, orow, lane);
+    return;
+  }
   float acc[DD];
 #pragma unroll
   for (int dd = 0; dd < DD; ++dd) acc[dd] = 0.f;
