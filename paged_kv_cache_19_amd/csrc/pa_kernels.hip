@@ -14,10 +14,13 @@
 //   reshape_and_cache_kernel     bit copy of new K/V into their slots
 //   reshape_and_cache_fp8_kernel the same into e4m3 pools (per-block scales)
 //   copy_blocks_kernel           whole-block copies (copy-on-write, swap)
-//   decode_streamk_kernel<D, FP8> balanced split-K decode (bf16 or e4m3
+//   decode_streamk_kernel<D, FP8, PREFIX>
+//                                balanced split-K decode (bf16 or e4m3
 //                                cache); QK^T and PV on
 //                                v_mfma_f32_16x16x32_bf16, online softmax in
-//                                fp32 with cross-lane max/sum
+//                                fp32 with cross-lane max/sum; with PREFIX,
+//                                a shared prefix read once per group of
+//                                sequences
 //   merge_streamk_kernel         log-sum-exp merge of its pieces
 //   prefill_kernel<D>            causal query chunks on
 //                                v_mfma_f32_32x32x16_bf16, K/V staged in LDS
