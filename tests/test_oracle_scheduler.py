@@ -9,11 +9,21 @@
   (tables [0, 1, 3] / [0, 2, 4], block 0 shared with reference count 2) is
   the page's.
 * FNV-1a 64-bit against its published test vectors.
-* A fuzz run with token ids written into a simulated pool through the
-  emitted slots: every scheduled sequence reads back exactly its own tokens
-  through its table (prefix hits included), budgets hold, invariants hold.
+* A fuzz run that writes, through the emitted slots, what a slot's K/V
+  depends on -- the token and every token before it in its sequence -- into
+  a simulated pool: every scheduled sequence reads back exactly its own
+  prefixes through its table (prefix hits included), budgets hold,
+  invariants hold.  One stream draws prompts from a few whole blocks, so
+  that equal blocks after different earlier blocks are common.
+* Prefix reuse keys a block by everything before it ("Tech Radar ...",
+  section "Prefix Caching: Radix Tree vs. Hash-Based Indexing": a tree node
+  is reached only through its ancestors): a block whose tokens match a
+  cached block that follows different earlier blocks is not reused.  A
+  prompt whose every block is cached still computes its last token (its
+  logits are needed), in a block of its own.
 Planted mistakes (budget not reduced by decode rows, a hit on a partial
-block, a wrong slot offset) fail.
+block, a wrong slot offset, a key without its parent, a hit on the block
+holding the last token) fail.
 """
 import json
 import os
@@ -41,8 +51,9 @@ def _sample(req_id, pos):
 
 
 def run(s, steps, pool=None, B=None, check=True):
-    """Drive ``steps`` steps; with ``pool`` (dict slot -> (req, pos, token)),
-    write token ids through the slots and check reads through tables."""
+    """Drive ``steps`` steps; with ``pool`` (dict slot -> the tokens its K/V
+    was computed from), write through the slots and check reads through
+    tables."""
     out = []
     for _ in range(steps):
         batch = s.step()
@@ -52,11 +63,12 @@ def run(s, steps, pool=None, B=None, check=True):
             r = by_id[e.req_id]
             first = e.seq_len - e.q_len
             if pool is not None:
+                # a slot's K/V is a function of its token and all earlier ones
                 for j, slot in enumerate(e.slots):
-                    pool[slot] = r.tokens[first + j]
+                    pool[slot] = tuple(r.tokens[:first + j + 1])
                 for p in range(e.seq_len):
                     blk = e.table[p // B]
-                    assert pool.get(blk * B + p % B) == r.tokens[p], (e.req_id, p)
+                    assert pool.get(blk * B + p % B) == tuple(r.tokens[:p + 1]), (e.req_id, p)
         sampled = {e.req_id: _sample(e.req_id, e.seq_len) for e in batch.entries}
         s.update(batch, sampled)
         if check:
@@ -125,18 +137,31 @@ def test_walkthrough_reached_by_prefix_reuse():
     assert [pool[2 * B + o] for o in range(4)] == Bq.tokens[4:8]
 
 
-def _fuzz(seed, steps=60, num_blocks=48, max_new=10):
+def block_prompt(rng, vocab_blocks, B):
+    """A prompt of 1-4 whole blocks drawn from ``vocab_blocks`` plus 0-B
+    loose tokens: the same block often follows different earlier blocks."""
+    prompt = []
+    for _ in range(rng.randrange(1, 5)):
+        prompt += rng.choice(vocab_blocks)
+    return prompt + [rng.randrange(50) for _ in range(rng.randrange(0, B + 1))]
+
+
+def _fuzz(seed, steps=60, num_blocks=48, max_new=10, block_vocab=False):
     rng = random.Random(seed)
     B = 4
     s = sch.Scheduler(num_blocks=num_blocks, block_size=B, token_budget=24, chunk_tokens=8,
                       free_order=rng.sample(range(num_blocks), num_blocks))
     prefixes = [[rng.randrange(50) for _ in range(rng.randrange(1, 14))] for _ in range(3)]
+    vocab_blocks = [[rng.randrange(50) for _ in range(B)] for _ in range(3)]
     pool = {}
     nid = 0
     for _ in range(steps):
         for _ in range(rng.randrange(0, 3)):
-            pre = rng.choice(prefixes) if rng.random() < 0.6 else []
-            prompt = pre + [rng.randrange(50) for _ in range(rng.randrange(1, 12))]
+            if block_vocab:
+                prompt = block_prompt(rng, vocab_blocks, B)
+            else:
+                pre = rng.choice(prefixes) if rng.random() < 0.6 else []
+                prompt = pre + [rng.randrange(50) for _ in range(rng.randrange(1, 12))]
             s.add_request(nid, prompt, max_new_tokens=rng.randrange(1, max_new))
             nid += 1
         batch = run(s, 1, pool, B)[0]
@@ -149,6 +174,72 @@ def _fuzz(seed, steps=60, num_blocks=48, max_new=10):
 @pytest.mark.parametrize("seed", range(6))
 def test_fuzz_tokens_read_back_through_tables(seed):
     _fuzz(seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_repeated_blocks_read_back_their_prefixes(seed):
+    _fuzz(seed, block_vocab=True)
+
+
+X, Y, Z = [1, 2, 3, 4], [5, 6, 7, 8], [9, 10, 11, 12]
+
+
+def _admit_alone(s, req_id, prompt):
+    """Admit one request and run its prefill to the end (one step each)."""
+    s.add_request(req_id, prompt, max_new_tokens=1)
+    first = None
+    while True:
+        batch = s.step()
+        e = next(e for e in batch.entries if e.req_id == req_id)
+        first = first or e
+        r = next(r for r in s.running if r.req_id == req_id)
+        s.update(batch, {x.req_id: 0 for x in batch.entries})
+        s.check_invariants()
+        if r.num_computed >= r.prompt_len:
+            return first, list(r.table)
+
+
+def prefix_key_chain_case(s):
+    """Three prompts share block Y after different first blocks (X, then Z,
+    then Z again).  Returns the tables and first entries."""
+    a_entry, a = _admit_alone(s, 0, X + Y + [13])
+    c_entry, c = _admit_alone(s, 1, Z + Y + [14])
+    d_entry, d = _admit_alone(s, 2, Z + Y + [15])
+    e_entry, e = _admit_alone(s, 3, X + Y + [16])
+    return (a_entry, a), (c_entry, c), (d_entry, d), (e_entry, e)
+
+
+def check_prefix_key_chain(results, B=4):
+    (a_entry, a), (c_entry, c), (d_entry, d), (e_entry, e) = results
+    # Z + Y: block Y follows Z, not X -- no hit at all, every token computed
+    assert c_entry.q_len == 2 * B + 1 and c[1] != a[1]
+    # Z + Y again: both blocks are the ones computed after Z
+    assert d_entry.q_len == 1 and d[:2] == c[:2] and d[1] != a[1]
+    # X + Y again: the blocks computed after X
+    assert e_entry.q_len == 1 and e[:2] == a[:2]
+
+
+def test_prefix_key_names_the_whole_prefix():
+    s = sch.Scheduler(num_blocks=32, block_size=4, token_budget=64, chunk_tokens=64)
+    check_prefix_key_chain(prefix_key_chain_case(s))
+
+
+def full_prompt_case(s):
+    """A prompt of exactly two blocks, cached, then asked for again."""
+    _, a = _admit_alone(s, 0, X + Y)
+    b_entry, b = _admit_alone(s, 1, X + Y)
+    return a, b_entry, b
+
+
+def check_full_prompt(a, b_entry, b, B=4):
+    # the block holding the last token is computed again, in a block of its own
+    assert b_entry.q_len == B and b_entry.seq_len == 2 * B
+    assert b[0] == a[0] and b[1] != a[1]
+
+
+def test_fully_cached_prompt_computes_its_last_token():
+    s = sch.Scheduler(num_blocks=32, block_size=4, token_budget=64, chunk_tokens=64)
+    check_full_prompt(*full_prompt_case(s))
 
 
 def test_fuzz_under_memory_pressure_preempts_and_recovers():
@@ -202,20 +293,56 @@ def _bad_slots(self, req, c):
     return e
 
 
+def _lookup_uncapped(self, req):
+    """Hits may cover the block holding the prompt's last token."""
+    hits, parent = [], sch.FNV_OFFSET
+    for i in range(len(req.tokens) // self.B):
+        k = sch.block_key(parent, req.tokens[i * self.B:(i + 1) * self.B])
+        b = self.block_of_key.get(k)
+        if b is None:
+            break
+        hits.append((b, k))
+        parent = k
+    return hits
+
+
+def _flat_key(parent, tokens):
+    """A block keyed by its own tokens only (parent dropped)."""
+    return _orig_block_key(sch.FNV_OFFSET, tokens)
+
+
 _orig_step = sch.Scheduler.step
 _orig_lookup = sch.Scheduler._lookup
 _orig_schedule = sch.Scheduler._schedule
+_orig_block_key = sch.block_key
+
+
+def _all_pins():
+    test_chunk_formula_worked_example()
+    for seed in range(6):
+        _fuzz(seed)
+        _fuzz(seed, block_vocab=True)
+    test_prefix_key_names_the_whole_prefix()
+    test_fully_cached_prompt_computes_its_last_token()
 
 
 @pytest.mark.parametrize("name,bad", [("step", _bad_budget), ("_lookup", _bad_lookup),
-                                      ("_schedule", _bad_slots)])
+                                      ("_schedule", _bad_slots),
+                                      ("_lookup", _lookup_uncapped)])
 def test_planted_scheduler_mistake_fails(monkeypatch, name, bad):
     monkeypatch.setattr(sch.Scheduler, name, bad)
-    failed = False
-    try:
-        test_chunk_formula_worked_example()
+    with pytest.raises((AssertionError, KeyError, IndexError, StopIteration)):
+        _all_pins()
+
+
+def test_planted_flat_block_key_fails(monkeypatch):
+    monkeypatch.setattr(sch, "block_key", _flat_key)
+    with pytest.raises(AssertionError):
+        test_prefix_key_names_the_whole_prefix()
+    with pytest.raises(AssertionError):
         for seed in range(6):
-            _fuzz(seed)
-    except (AssertionError, KeyError, IndexError):
-        failed = True
-    assert failed
+            _fuzz(seed, block_vocab=True)
+
+
+def test_pins_pass_unmutated():
+    _all_pins()

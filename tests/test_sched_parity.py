@@ -104,6 +104,59 @@ def test_random_streams_match(seed, num_blocks, max_new):
     assert (w, r, f) == (len(ref.waiting), len(ref.running), len(ref.finished))
 
 
+def _admit_pair(ref, nat, req_id, prompt):
+    """Admit one request on both builders and run its prefill to the end;
+    returns the oracle's first entry and the request's table."""
+    ref.add_request(req_id, prompt, 1)
+    nat.add_request(req_id, prompt, 1)
+    first = None
+    while True:
+        b = _compare_step(ref, nat)
+        e = next(e for e in b.entries if e.req_id == req_id)
+        first = first or e
+        r = next(r for r in ref.running if r.req_id == req_id)
+        if r.num_computed >= r.prompt_len:
+            return first, list(r.table)
+
+
+def test_prefix_key_chain_native():
+    """Equal blocks after different first blocks are not shared, on both
+    builders (the oracle's pin of the chained key, replayed natively)."""
+    from tests.test_oracle_scheduler import X, Y, Z, check_prefix_key_chain
+    ref, nat = _pair(32, 4, 64, 64)
+    res = [_admit_pair(ref, nat, i, p)
+           for i, p in enumerate([X + Y + [13], Z + Y + [14], Z + Y + [15], X + Y + [16]])]
+    check_prefix_key_chain(res)
+
+
+def test_fully_cached_prompt_native():
+    from tests.test_oracle_scheduler import X, Y, check_full_prompt
+    ref, nat = _pair(32, 4, 64, 64)
+    _, a = _admit_pair(ref, nat, 0, X + Y)
+    b_entry, b = _admit_pair(ref, nat, 1, X + Y)
+    check_full_prompt(a, b_entry, b)
+
+
+@pytest.mark.parametrize("seed,num_blocks", [(s, 48) for s in range(3)] + [(s, 14) for s in range(3)])
+def test_repeated_block_streams_match(seed, num_blocks):
+    """Prompts built from a few whole blocks: the same block after different
+    earlier blocks is common, so a key that ignored its parent would show."""
+    from tests.test_oracle_scheduler import block_prompt
+    rng = random.Random(100 + seed)
+    B = 4
+    ref, nat = _pair(num_blocks, B, 24, 8, rng.sample(range(num_blocks), num_blocks))
+    vocab_blocks = [[rng.randrange(50) for _ in range(B)] for _ in range(3)]
+    nid = 0
+    for _ in range(80):
+        for _ in range(rng.randrange(0, 3)):
+            prompt = block_prompt(rng, vocab_blocks, B)
+            mn = rng.randrange(1, 30)
+            ref.add_request(nid, prompt, mn)
+            nat.add_request(nid, prompt, mn)
+            nid += 1
+        _compare_step(ref, nat)
+
+
 def test_native_argument_errors():
     lib = binding.lib()
     assert not lib.pa_sched_create(0, 16, 64, 64, None)
