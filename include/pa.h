@@ -52,6 +52,30 @@
  * Supported: dtype PA_F32 or PA_BF16; head_dim 64 or 128; block_size a
  * power of two from 1 to 64; H_q % H_kv == 0 with 1 <= H_q / H_kv <= 16;
  * kv_split_tokens 0 (auto) or a positive multiple of 64.
+ *
+ * Where this ABI departs from the plainest reading of the pages
+ * -------------------------------------------------------------
+ * The pages fix no intra-block layout and no argument list; the one a
+ * caller would first expect is K and V both token-major, [NB, H_kv, B, D],
+ * and the three calls with only the arguments the method names.  Here:
+ *  - v_cache is head_dim-major, [NB, H_kv, D, B].  A lane then loads 8
+ *    consecutive tokens of one head_dim column as one 16-byte load, which is
+ *    the B operand of the P.V matrix instruction as it stands.  K stays
+ *    token-major.  A caller holding token-major V pools must transpose each
+ *    block once (torch: v.transpose(2, 3).contiguous()) or fill the pool
+ *    through pa_reshape_and_cache, which writes this layout.  Passing a
+ *    token-major V pool is NOT detected by the library (its size is the
+ *    same) and gives wrong attention; the Python binding refuses it by
+ *    shape whenever B != D.
+ *  - pa_decode and pa_chunked_prefill take two more arguments:
+ *    block_refcounts (a cache hint, may be NULL) and kv_split_tokens
+ *    (0 = balanced; the workspace queries take it too, and the value must
+ *    match).
+ *  - dtype is passed as int32_t and the stream as void* (a hipStream_t), so
+ *    this header needs no HIP header.
+ *  - Added entry points: pa_compute_slot_mapping (the slot step on the
+ *    device), pa_version, the e4m3 cache calls, pa_decode_shared_prefix and
+ *    the whole-block copies.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -328,8 +352,10 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  * PA_ERR_INDEX, under PA_CHECK=1; otherwise results for a batch that breaks
  * it are undefined, but every access stays in bounds).  query and out: bf16
  * [num_seqs, num_q_heads, head_dim].  block_size >= 8 (>= 16 for e4m3);
- * num_seqs + ceil(num_seqs / group) <= 4096, else
- * PA_ERR_UNSUPPORTED.  prefix_blocks == 0 runs pa_decode's balanced path.
+ * when the prefix holds at least one whole step, num_seqs +
+ * ceil(num_seqs / group) <= 4096, else PA_ERR_UNSUPPORTED.  A prefix shorter
+ * than one step (prefix_blocks == 0 included) runs pa_decode's (e4m3:
+ * pa_decode_fp8's) path with that call's limits.
  * Other arguments, errors and the workspace ownership as for pa_decode and
  * pa_decode_fp8.
  */

@@ -114,6 +114,63 @@ def _dtype(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _same_device(*ts) -> None:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
+def _want(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _pools(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """Shapes of a K/V pool pair: K [NB, H_kv, B, D] and V [NB, H_kv, D, B]
+    (the V pool keeps each head_dim row's B tokens contiguous).  Returns
+    (NB, H_kv, B, D).  A V pool laid out like K is refused whenever B != D;
+    with B == D the two layouts have one shape and only the caller can tell."""
+    _want(k_cache.dim() == 4 and v_cache.dim() == 4,
+          "k_cache and v_cache are 4-d pools [NB, H_kv, B, D] / [NB, H_kv, D, B]")
+    NB, Hkv, B, D = k_cache.shape
+    _want(tuple(v_cache.shape) == (NB, Hkv, D, B),
+          f"v_cache must be [NB, H_kv, D, B] = {(NB, Hkv, D, B)} for k_cache {tuple(k_cache.shape)}"
+          f", got {tuple(v_cache.shape)}")
+    _want(k_cache.dtype == v_cache.dtype, "k_cache and v_cache have different dtypes")
+    return NB, Hkv, B, D
+
+
+def _metadata(block_tables: torch.Tensor, seq_lens: torch.Tensor, num_seqs: int,
+              block_refcounts: Optional[torch.Tensor], num_blocks: int,
+              query_start_loc: Optional[torch.Tensor] = None) -> None:
+    _want(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == num_seqs,
+          f"block_tables must be int32 [{num_seqs}, max_blocks_per_seq]")
+    _want(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (num_seqs,),
+          f"seq_lens must be int32 [{num_seqs}]")
+    if query_start_loc is not None:
+        _want(query_start_loc.dtype == torch.int32
+              and tuple(query_start_loc.shape) == (num_seqs + 1,),
+              f"query_start_loc must be int32 [{num_seqs + 1}]")
+    if block_refcounts is not None:
+        _want(block_refcounts.dtype == torch.int32
+              and tuple(block_refcounts.shape) == (num_blocks,),
+              f"block_refcounts must be int32 [{num_blocks}]")
+
+
+def _rows(query: torch.Tensor, out: Optional[torch.Tensor], Hkv: int, D: int) -> None:
+    _want(query.dim() == 3 and query.shape[2] == D, f"query must be [T, H_q, {D}]")
+    _want(query.shape[1] % Hkv == 0, f"num_q_heads {query.shape[1]} is not a multiple of {Hkv}")
+    if out is not None:
+        _want(out.shape == query.shape and out.dtype == query.dtype,
+              "out must have the shape and dtype of query")
+
+
+def _workspace(ws: Optional[torch.Tensor]) -> None:
+    if ws is not None:
+        _want(ws.dtype == torch.uint8 and ws.dim() == 1, "workspace is a 1-d uint8 tensor")
+
+
 def status_string(status: int) -> str:
     return lib().pa_status_string(status).decode()
 
@@ -127,8 +184,13 @@ def compute_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor,
                          num_tokens: Optional[int] = None, out: Optional[torch.Tensor] = None,
                          stream=None) -> torch.Tensor:
     S = seq_lens.numel()
+    _metadata(block_tables, seq_lens, S, None, 0, query_start_loc)
+    _same_device(block_tables, seq_lens, query_start_loc, out)
     if num_tokens is None:
         num_tokens = S if query_start_loc is None else int(query_start_loc[-1].item())
+    if out is not None:
+        _want(out.dtype == torch.int64 and tuple(out.shape) == (num_tokens,),
+              f"slot_mapping out must be int64 [{num_tokens}]")
     if out is None:
         out = torch.empty(num_tokens, dtype=torch.int64, device=seq_lens.device)
     _check("pa_compute_slot_mapping", lib().pa_compute_slot_mapping(
@@ -139,8 +201,17 @@ def compute_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor,
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
                       v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
-    T, H, D = key.shape
-    NB, _, B, _ = k_cache.shape
+    NB, Hkv, B, D = _pools(k_cache, v_cache)
+    _want(key.dim() == 3 and tuple(key.shape[1:]) == (Hkv, D),
+          f"key must be [T, {Hkv}, {D}] for these pools")
+    _want(value.shape == key.shape, "value must have the shape of key")
+    _want(key.dtype == value.dtype == k_cache.dtype,
+          f"key, value and the pools must share one dtype ({key.dtype}, {value.dtype}, "
+          f"{k_cache.dtype})")
+    T, H = key.shape[0], Hkv
+    _want(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,),
+          f"slot_mapping must be int64 [{T}]")
+    _same_device(key, value, k_cache, v_cache, slot_mapping)
     _check("pa_reshape_and_cache", lib().pa_reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, H, D, B,
         NB, _dtype(key), _stream(stream)))
@@ -169,8 +240,14 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            kv_split_tokens: int = 0, block_refcounts: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
-    S, Hq, D = query.shape
-    NB, Hkv, B, _ = k_cache.shape
+    NB, Hkv, B, D = _pools(k_cache, v_cache)
+    _rows(query, out, Hkv, D)
+    _want(query.dtype == k_cache.dtype,
+          f"query and the pools must share one dtype ({query.dtype}, {k_cache.dtype})")
+    S, Hq = query.shape[0], query.shape[1]
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _workspace(workspace)
+    _same_device(query, k_cache, v_cache, block_tables, seq_lens, block_refcounts, out, workspace)
     if out is None:
         out = torch.empty_like(query)
     if workspace is None:  # needs no initialisation
@@ -191,9 +268,16 @@ def chunked_prefill(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                     block_refcounts: Optional[torch.Tensor] = None,
                     out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    T, Hq, D = query.shape
-    NB, Hkv, B, _ = k_cache.shape
+    NB, Hkv, B, D = _pools(k_cache, v_cache)
+    _rows(query, out, Hkv, D)
+    _want(query.dtype == k_cache.dtype,
+          f"query and the pools must share one dtype ({query.dtype}, {k_cache.dtype})")
+    T, Hq = query.shape[0], query.shape[1]
     S = seq_lens.numel()
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB, query_start_loc)
+    _workspace(workspace)
+    _same_device(query, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                 block_refcounts, out, workspace)
     if out is None:
         out = torch.empty_like(query)
     if workspace is None:  # needs no initialisation
@@ -227,6 +311,9 @@ def _block_bytes(pool: torch.Tensor) -> int:
 def copy_blocks(pool: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
     """Copy-on-write inside one pool: block d = block s for every (s, d) row
     of the device int64 ``block_mapping`` [n, 2]."""
+    _want(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+          and block_mapping.shape[1] == 2, "block_mapping must be int64 [n, 2]")
+    _same_device(pool, block_mapping)
     _check("pa_copy_blocks", lib().pa_copy_blocks(
         _ptr(pool), _ptr(block_mapping), block_mapping.shape[0], _block_bytes(pool),
         pool.shape[0], _stream(stream)))
@@ -238,6 +325,9 @@ def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor, block_mapping: t
     ``dst_pool`` = block s of ``src_pool`` for every (s, d) row."""
     if _block_bytes(dst_pool) != _block_bytes(src_pool):
         raise ValueError("pools with different block sizes")
+    _want(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+          and block_mapping.shape[1] == 2, "block_mapping must be int64 [n, 2]")
+    _want(block_mapping.is_cuda, "block_mapping is a device tensor")
     _check("pa_swap_blocks", lib().pa_swap_blocks(
         _pool_ptr(dst_pool), _pool_ptr(src_pool), _ptr(block_mapping), block_mapping.shape[0],
         _block_bytes(dst_pool), dst_pool.shape[0], src_pool.shape[0], _stream(stream)))
@@ -255,17 +345,29 @@ def _f32(t: torch.Tensor) -> None:
         raise ValueError("scales are float32 [num_blocks, num_kv_heads]")
 
 
+def _fp8_pools(k_cache, v_cache, k_scales, v_scales):
+    """Shapes of an e4m3 pool pair and its scales; returns (NB, H_kv, B, D)."""
+    NB, Hkv, B, D = _pools(k_cache, v_cache)
+    _fp8_pool(k_cache)
+    _f32(k_scales)
+    _f32(v_scales)
+    _want(tuple(k_scales.shape) == (NB, Hkv) and tuple(v_scales.shape) == (NB, Hkv),
+          f"k_scales and v_scales must be float32 [{NB}, {Hkv}]")
+    return NB, Hkv, B, D
+
+
 def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
                           v_cache: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
                           slot_mapping: torch.Tensor, stream=None) -> None:
-    T, H, D = key.shape
-    NB, _, B, _ = k_cache.shape
+    NB, H, B, D = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
     if key.dtype != torch.bfloat16 or value.dtype != torch.bfloat16:
         raise ValueError("key/value are bf16")
-    _fp8_pool(k_cache)
-    _fp8_pool(v_cache)
-    _f32(k_scales)
-    _f32(v_scales)
+    _want(key.dim() == 3 and tuple(key.shape[1:]) == (H, D) and value.shape == key.shape,
+          f"key and value must be [T, {H}, {D}] for these pools")
+    T = key.shape[0]
+    _want(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,),
+          f"slot_mapping must be int64 [{T}]")
+    _same_device(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping)
     _check("pa_reshape_and_cache_fp8", lib().pa_reshape_and_cache_fp8(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
         _ptr(slot_mapping), T, H, D, B, NB, _stream(stream)))
@@ -285,14 +387,15 @@ def decode_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                block_refcounts: Optional[torch.Tensor] = None,
                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
-    S, Hq, D = query.shape
-    NB, Hkv, B, _ = k_cache.shape
+    NB, Hkv, B, D = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
     if query.dtype != torch.bfloat16:
         raise ValueError("the fp8 decode takes a bf16 query")
-    _fp8_pool(k_cache)
-    _fp8_pool(v_cache)
-    _f32(k_scales)
-    _f32(v_scales)
+    _rows(query, out, Hkv, D)
+    S, Hq = query.shape[0], query.shape[1]
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _workspace(workspace)
+    _same_device(query, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                 block_refcounts, out, workspace)
     if out is None:
         out = torch.empty_like(query)
     if workspace is None:  # needs no initialisation
@@ -326,17 +429,21 @@ def decode_shared_prefix(query: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     """pa_decode (bf16 pools) or pa_decode_fp8 (e4m3 pools, with k_scales and
     v_scales) for a batch whose tables all start with the same prefix_blocks
     blocks."""
-    S, Hq, D = query.shape
-    NB, Hkv, B, _ = k_cache.shape
     if query.dtype != torch.bfloat16:
         raise ValueError("the shared-prefix decode takes a bf16 query")
     if (k_scales is None) != (v_scales is None):
         raise ValueError("pass both k_scales and v_scales (e4m3 pools) or neither")
     if k_scales is not None:
-        _fp8_pool(k_cache)
-        _fp8_pool(v_cache)
-        _f32(k_scales)
-        _f32(v_scales)
+        NB, Hkv, B, D = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    else:
+        NB, Hkv, B, D = _pools(k_cache, v_cache)
+        _want(k_cache.dtype == torch.bfloat16, "without scales the pools are bf16")
+    _rows(query, out, Hkv, D)
+    S, Hq = query.shape[0], query.shape[1]
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _workspace(workspace)
+    _same_device(query, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                 block_refcounts, out, workspace)
     if out is None:
         out = torch.empty_like(query)
     if workspace is None:  # needs no initialisation

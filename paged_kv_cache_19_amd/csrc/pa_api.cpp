@@ -631,8 +631,12 @@ int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
   if ((int64_t)prefix_blocks * block_size > max_seq_len ||
       prefix_blocks > max_blocks_per_seq)
     return PA_ERR_SHAPE;
-  if (num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
-      num_q_heads / num_kv_heads <= 16) {
+  // Without a whole prefix step there is no prefix entry: pa_decode's (or
+  // pa_decode_fp8's) limits apply, including the bf16 fixed-split fallback.
+  const int pstep = fp8 ? 64 : 32;
+  const int64_t prefix_keys = block_size > 0 ? (int64_t)prefix_blocks * block_size / pstep * pstep : 0;
+  if (prefix_keys > 0 && num_q_heads > 0 && num_kv_heads > 0 &&
+      num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 16) {
     const int spg = 16 * pa::prefix_tiles(fp8) / (num_q_heads / num_kv_heads);
     if ((int64_t)num_seqs + (num_seqs + spg - 1) / spg > kMaxBalancedSeqs)
       return PA_ERR_UNSUPPORTED;

@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import math
 import random
-from typing import List, Optional, Sequence
+from typing import List, Optional
 
 import torch
 
@@ -43,36 +43,21 @@ def bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-def sample_rows(wl: workloads.Workload, max_seqs: Optional[int], seed: int = 0) -> List[int]:
-    """Packed row indices to check against the oracle: every row of up to
-    ``max_seqs`` sequences (always the shortest and the longest), and for
-    query chunks the first/last rows, rows around block boundaries and a
-    random handful."""
-    rng = random.Random(seed)
+def sample_rows(wl: workloads.Workload, max_seqs: Optional[int] = None,
+                seed: int = 0) -> List[int]:
+    """Packed row indices to check against the oracle.  By default every row
+    of every sequence.  With ``max_seqs``, every row of that many sequences:
+    the shortest, the longest, the last and a seeded random choice of the
+    rest (for batches whose every row the oracle cannot afford)."""
     S = wl.num_seqs
     qsl = wl.query_start_loc()
     if max_seqs is None or max_seqs >= S:
-        seqs = list(range(S))
-    else:
-        lens = wl.seq_lens
-        seqs = {lens.index(min(lens)), lens.index(max(lens))}
-        seqs |= set(rng.sample(range(S), max_seqs - 2))
-        seqs = sorted(seqs)
-    rows = []
-    B = wl.shape.block_size
-    for s in seqs:
-        n = wl.q_lens[s]
-        if n <= 48:
-            rows += list(range(qsl[s], qsl[s] + n))
-            continue
-        pick = {0, 1, 2, n - 3, n - 2, n - 1}
-        ctx = wl.seq_lens[s] - n
-        for j in range(n):
-            if (ctx + j) % B in (0, B - 1) and rng.random() < 0.3:
-                pick.add(j)
-        pick |= set(rng.sample(range(n), 8))
-        rows += [qsl[s] + j for j in sorted(pick)]
-    return rows
+        return list(range(qsl[S]))
+    rng = random.Random(seed)
+    lens = wl.seq_lens
+    seqs = {lens.index(min(lens)), lens.index(max(lens)), S - 1}
+    seqs |= set(rng.sample(range(S), max(0, max_seqs - len(seqs))))
+    return [r for s in sorted(seqs) for r in range(qsl[s], qsl[s + 1])]
 
 
 def run_and_compare(wl: workloads.Workload, kv_split_tokens: int = 0,

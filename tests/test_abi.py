@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from paged_kv_cache_19_amd import binding
 from tests.conftest import ROOT
@@ -161,6 +162,20 @@ def test_shared_prefix_decode_rejects_bad_arguments(lib, kw, code):
     assert _shared(lib, **kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=4000, pb=0), -5),                 # no prefix: pa_decode's limits (fails on ws only)
+    (dict(S=4000, pb=1), -5),                 # 16 keys < one 32-key step: no prefix entry
+    (dict(S=5000, pb=0), -5),                 # bf16 beyond 4,096: the fixed-split path
+    (dict(S=4000, pb=3, ks=FAKE, vs=FAKE), -5),            # 48 keys < 64: fp8 pa_decode path,
+    (dict(S=5000, pb=0, ks=FAKE, vs=FAKE, ws=FAKE), -4),   # which stops at 4,096 sequences
+])
+def test_shared_prefix_without_a_whole_step_takes_decode_limits(lib, kw, code):
+    """A prefix shorter than one key step adds no prefix entries, so the
+    entry limit is pa_decode's (bf16) or pa_decode_fp8's (e4m3)."""
+    kw.setdefault("ws", None)
+    assert _shared(lib, **kw) == code
+
+
 def test_shared_prefix_decode_empty_batch_is_a_no_op(lib):
     assert _shared(lib, S=0, out=None) == 0
 
@@ -184,3 +199,65 @@ def test_block_copy_entry_points_reject_bad_arguments(lib):
     assert lib.pa_swap_blocks(FAKE, FAKE, m, 2, 64, 8, 8, None) == -2   # same pool: use copy
     assert lib.pa_swap_blocks(None, FAKE, m, 2, 64, 8, 8, None) == -1
     assert lib.pa_swap_blocks(FAKE, ctypes.c_void_p(32), m, 2, 64, 8, 0, None) == -2
+
+
+def _cpu_case(dtype=None, D=64, B=16, Hkv=2, Hq=8, NB=10, S=3):
+    dtype = dtype or torch.bfloat16
+    return dict(
+        q=torch.zeros(S, Hq, D, dtype=dtype), kc=torch.zeros(NB, Hkv, B, D, dtype=dtype),
+        vc=torch.zeros(NB, Hkv, D, B, dtype=dtype), bt=torch.zeros(S, 4, dtype=torch.int32),
+        lens=torch.ones(S, dtype=torch.int32), key=torch.zeros(S, Hkv, D, dtype=dtype),
+        slots=torch.zeros(S, dtype=torch.int64))
+
+
+@pytest.mark.parametrize("mutate,match", [
+    (lambda c: c.update(vc=c["vc"].transpose(2, 3).contiguous()), "v_cache must be"),
+    (lambda c: c.update(kc=c["kc"].float(), vc=c["vc"].float()), "share one dtype"),
+    (lambda c: c.update(q=c["q"][:, :, :32].contiguous()), "query must be"),
+    (lambda c: c.update(bt=c["bt"].long()), "block_tables must be int32"),
+    (lambda c: c.update(lens=c["lens"][:2].contiguous()), "seq_lens must be int32"),
+])
+def test_binding_decode_checks_shapes_and_dtypes(lib, mutate, match):
+    """Mismatches between query, pools and metadata are refused before any
+    pointer reaches the library: a token-major V pool, a query of another
+    dtype, a wrong head_dim, int64 tables, short seq_lens."""
+    c = _cpu_case()
+    mutate(c)
+    with pytest.raises(ValueError, match=match):
+        binding.decode(c["q"], c["kc"], c["vc"], c["bt"], c["lens"], 64, 0.125,
+                       out=torch.empty_like(c["q"]))
+
+
+@pytest.mark.parametrize("mutate,match", [
+    (lambda c: c.update(key=c["key"].float()), "share one dtype"),
+    (lambda c: c.update(key=c["key"][:, :1].contiguous()), "key must be"),
+    (lambda c: c.update(slots=c["slots"].int()), "slot_mapping must be int64"),
+    (lambda c: c.update(vc=c["vc"][:, :, :32].contiguous()), "v_cache must be"),
+])
+def test_binding_cache_write_checks_shapes_and_dtypes(lib, mutate, match):
+    """An fp32 key into a bf16 pool (which would write past the pool's end),
+    a key with the wrong head count, int32 slots and a wrong V pool are
+    refused."""
+    c = _cpu_case()
+    mutate(c)
+    with pytest.raises(ValueError, match=match):
+        binding.reshape_and_cache(c["key"], c["key"].clone(), c["kc"], c["vc"], c["slots"])
+
+
+def test_binding_chunked_prefill_checks_query_start_loc(lib):
+    c = _cpu_case()
+    qsl = torch.tensor([0, 1, 2], dtype=torch.int32)          # needs S + 1 = 4 entries
+    with pytest.raises(ValueError, match="query_start_loc must be"):
+        binding.chunked_prefill(c["q"], c["kc"], c["vc"], c["bt"], c["lens"], qsl, 64, 1, 0.125)
+
+
+def test_binding_fp8_checks_scales(lib):
+    c = _cpu_case()
+    k8 = torch.zeros(10, 2, 16, 64, dtype=torch.uint8)
+    v8 = torch.zeros(10, 2, 64, 16, dtype=torch.uint8)
+    ks = torch.ones(10, 2)
+    with pytest.raises(ValueError, match="k_scales and v_scales must be"):
+        binding.decode_fp8(c["q"], k8, v8, ks, ks[:5].contiguous(), c["bt"], c["lens"], 64, 0.125)
+    with pytest.raises(ValueError, match="v_cache must be"):
+        binding.decode_fp8(c["q"], k8, v8.transpose(2, 3).contiguous(), ks, ks, c["bt"],
+                           c["lens"], 64, 0.125)

@@ -70,11 +70,12 @@ def _run_fp8(wl, max_seqs=None, refcounts=True, check_write=True):
     return out, err
 
 
-@pytest.mark.parametrize("cfg,max_seqs", [(2, None), (3, 10), (4, 16), (6, 4), (7, 10)])
-def test_fp8_workload_parity(cfg, max_seqs):
+@pytest.mark.parametrize("cfg", [2, 3, 4, 6, 7])
+def test_fp8_workload_parity(cfg):
+    """Every row of every sequence of the full-size workloads."""
     log(f"[fp8] workload {cfg}")
     wl = workloads.make_workload(cfg, device="cuda", kv_fp8=True)
-    _, err = _run_fp8(wl, max_seqs=max_seqs)
+    _, err = _run_fp8(wl)
     log(f"[fp8] workload {cfg}: max abs err {err:.3e}")
     assert err <= TOL
     del wl

@@ -6,7 +6,10 @@ pa_decode_fp8, and sequences plus one prefix entry per group for
 pa_decode_shared_prefix.  At the limit the calls must still match the
 oracle; one past it, bf16 pa_decode runs its fixed-split kernel (same
 result) and the e4m3 and shared-prefix calls refuse with
-PA_ERR_UNSUPPORTED.  Short sequences keep the oracle's sample cheap.
+PA_ERR_UNSUPPORTED.  Short sequences keep the oracle cheap enough to check
+every row.  At 4,096 sequences the balanced decode is also compared row by
+row with the fixed-split kernel (64-key splits), which cuts every row at
+other places.
 """
 import numpy as np
 import pytest
@@ -31,8 +34,17 @@ def test_decode_at_the_sequence_limit(num_seqs):
     log(f"[limits] pa_decode with {num_seqs} sequences")
     wl = workloads.make_workload(2, seed=61, device="cuda", seq_lens=_lens(num_seqs, 61),
                                  shape=SHAPE)
-    _, err = run_and_compare(wl, max_seqs=40)
+    out, err = run_and_compare(wl)
     assert err <= TOL[workloads.BF16]
+    if num_seqs == 4096:
+        t = wl.tensors
+        fixed = binding.decode(t["query"], t["k_cache"], t["v_cache"],
+                               wl.block_tables_tensor("cuda"), wl.seq_lens_tensor("cuda"),
+                               wl.max_seq_len, wl.scale, kv_split_tokens=64)
+        torch.cuda.synchronize()
+        diff = (out.float() - fixed.float()).abs().max().item()
+        log(f"[limits] balanced vs 64-key splits: max abs diff {diff:.3e}")
+        assert diff <= TOL[workloads.BF16]
     del wl
     torch.cuda.empty_cache()
 
@@ -42,7 +54,7 @@ def test_fp8_decode_at_the_sequence_limit():
     log("[limits] pa_decode_fp8 with 4096 sequences")
     wl = workloads.make_workload(2, seed=62, device="cuda", seq_lens=_lens(4096, 62),
                                  shape=SHAPE, kv_fp8=True)
-    _, err = _run_fp8(wl, max_seqs=40)
+    _, err = _run_fp8(wl)
     assert err <= 2e-2
     t = wl.tensors
     over = workloads.make_workload(2, seed=63, device="cuda", seq_lens=_lens(4097, 63),
@@ -66,7 +78,7 @@ def test_shared_prefix_decode_at_the_entry_limit():
     lens = _lens(3640, 64, lo=65, hi=260)
     wl = workloads.make_workload(2, seed=64, device="cuda", seq_lens=lens, shape=SHAPE,
                                  shared_prefix_tokens=64)
-    _, err, diff = _run(wl, 4, max_seqs=40)
+    _, err, diff = _run(wl, 4)
     assert err <= 2e-2 and diff <= 2e-2
     t = wl.tensors
     bt = wl.block_tables_tensor("cuda")
