@@ -19,7 +19,8 @@
  * ---------------------------------------
  *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
  *    library never allocates, frees or retains memory, holds no mutable
- *    global state and is re-entrant.
+ *    global state and is re-entrant -- except pa_decode_noalloc, whose
+ *    workspace is a static device array (see its comment).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns once it is enqueued, so
  *    stream order gives slot mapping -> cache write -> attention.
@@ -97,7 +98,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -4, /* valid but not implemented (head_dim, B, G)     */
   PA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required        */
   PA_ERR_INDEX = -6,       /* PA_CHECK=1 found bad device metadata           */
-  PA_ERR_HIP = -7          /* a HIP runtime call or a launch failed          */
+  PA_ERR_HIP = -7,         /* a HIP runtime call or a launch failed          */
+  PA_ERR_SCRATCH = -8      /* pa_decode_noalloc: needs more than its scratch */
 } pa_status;
 
 /* Human-readable name of a pa_status value (static string, never NULL). */
@@ -368,6 +370,37 @@ int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, int32_t prefix_blocks, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, hosts that forbid hipMalloc).
+ *
+ * pa_decode_noalloc -- pa_decode without a workspace argument: the
+ * workspace is a static device array of PA_NOALLOC_SCRATCH_BYTES (160 MiB,
+ * enough for the Llama-3-70B-layer decode batch of 128 sequences of up to
+ * 8,192 tokens, 64 query heads, which needs 145 MB) that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates and frees
+ * nothing (no hipMalloc, no allocating library call); the caller still
+ * passes every input and the output.  Its first call on a device looks up
+ * that device's copy of the array (with the device current).
+ * A batch whose workspace (pa_decode_workspace_bytes with the same
+ * arguments) exceeds the scratch returns PA_ERR_SCRATCH before anything is
+ * enqueued.  Every call on one GPU shares that GPU's scratch: calls that may
+ * overlap on one GPU (different streams, or different host threads without
+ * ordering) race and give undefined results; calls in one stream are
+ * ordered.  The scratch keeps the last call's contents, which no call reads
+ * (pa_decode's workspace needs no initialisation).  Arguments, results and
+ * other errors: as for pa_decode.
+ * ---------------------------------------------------------------------- */
+#define PA_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+
+int pa_decode_noalloc(void* out, const void* query, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t dtype, int32_t kv_split_tokens, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,10 @@ PA_BF16 = 1
 STATUS = {
     0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
     -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_INDEX", -7: "PA_ERR_HIP",
+    -8: "PA_ERR_SCRATCH",
 }
+PA_ERR_SCRATCH = -8
+NOALLOC_SCRATCH_BYTES = 160 * 1024 * 1024   # PA_NOALLOC_SCRATCH_BYTES of include/pa.h
 
 # (name, restype, argtypes) of every symbol include/pa.h declares.
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -54,6 +57,8 @@ SIGNATURES = {
     "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -258,6 +263,26 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S, max_seq_len, Hq, Hkv,
         D, B, NB, scale,
         _dtype(query), kv_split_tokens, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_noalloc(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                   scale: float, out: torch.Tensor, kv_split_tokens: int = 0,
+                   block_refcounts: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode with the library's static scratch as workspace: nothing is
+    allocated (the caller passes ``out``)."""
+    NB, Hkv, B, D = _pools(k_cache, v_cache)
+    _rows(query, out, Hkv, D)
+    _want(query.dtype == k_cache.dtype,
+          f"query and the pools must share one dtype ({query.dtype}, {k_cache.dtype})")
+    S, Hq = query.shape[0], query.shape[1]
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _same_device(query, k_cache, v_cache, block_tables, seq_lens, block_refcounts, out)
+    _check("pa_decode_noalloc", lib().pa_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S, max_seq_len, Hq, Hkv,
+        D, B, NB, scale, _dtype(query), kv_split_tokens, _stream(stream)))
     return out
 
 

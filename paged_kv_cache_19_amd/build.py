@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pa_kernels.hip", "pa_api.cpp", "pa_sched.cpp"]
+SOURCES = ["pa_kernels.hip", "pa_api.cpp", "pa_sched.cpp", "pa_noalloc.hip"]
 
 # Packed fp32 instructions are kept out of every kernel: hipcc must not
 # generate v_pk_{add,mul,fma}_f32 from ordinary float code on this target.

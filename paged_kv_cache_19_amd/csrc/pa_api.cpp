@@ -368,6 +368,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_INDEX: return "PA_ERR_INDEX: device metadata out of range (PA_CHECK)";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch failure";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the batch needs more workspace than pa_decode_noalloc's static "
+             "scratch (PA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown pa_status";
   }
 }

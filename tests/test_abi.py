@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding.SIGNATURES)
@@ -261,3 +261,19 @@ def test_binding_fp8_checks_scales(lib):
     with pytest.raises(ValueError, match="v_cache must be"):
         binding.decode_fp8(c["q"], k8, v8.transpose(2, 3).contiguous(), ks, ks, c["bt"],
                            c["lens"], 64, 0.125)
+
+
+def test_noalloc_refuses_a_batch_beyond_its_scratch(lib):
+    """pa_decode_noalloc checks the batch's workspace against its static
+    scratch before anything else touches the GPU."""
+    S, Hq, D, L, B = 1024, 64, 128, 8192, 16
+    assert lib.pa_decode_workspace_bytes(S, Hq, D, L, B, 0) > binding.NOALLOC_SCRATCH_BYTES
+    rc = lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 512, None, FAKE, S, L, Hq, 8, D, B,
+                               100000, 0.088, binding.PA_BF16, 0, None)
+    assert rc == binding.PA_ERR_SCRATCH
+    assert binding.status_string(rc).startswith("PA_ERR_SCRATCH")
+    # invalid sizes are pa_decode's errors, reported before the scratch is looked up
+    assert lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 512, None, FAKE, 4, 64, 8, 2, 96,
+                                 16, 64, 0.1, binding.PA_BF16, 0, None) == -4
+    assert lib.pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 512, None, FAKE, 4, 64, 8, 2, 128,
+                                 16, 64, 0.1, binding.PA_BF16, 100, None) == -2
