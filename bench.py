@@ -20,6 +20,13 @@ Prints ONE JSON line.  ``value`` is the step's KV-read throughput in GB/s
 HBM peak ride along.  ``roofline`` covers the attention call (the dominant
 one), timed with HIP events on the stream its kernels run on: HBM-bound for
 decode, MFMA-bound (bf16 dense peak) for the chunked-prefill mix.
+``roofline.ceiling`` is the second denominator: the read rate of a probe
+that gathers random 4 KiB tiles (one K or V tile of a block and KV head)
+from a 4 GiB pool with the decode's loads, measured in the same run.
+``cache_write`` times pa_reshape_and_cache (and the slot mapping) on their
+own.  By default the 256 MB Infinity Cache is flushed before every step,
+outside the timed events, so no step reads what the step before left there
+(a serving loop's next call on a layer comes after every other layer).
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 batch.
 """
@@ -39,7 +46,10 @@ METRIC = "paged-attention decode KV-read GB/s (% of HBM peak) and tokens/s, 1 MI
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "paged_kv_cache_19_amd", "csrc")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_llama3-70b-layer_hbm_counters.md")
+PROFILES = os.path.join(ROOT, "profiles")
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_19_amd", "libpa_probe.so")
+CEILING_TILE_BYTES = 4096
+CEILING_POOL_BYTES = 4 << 30
 
 SEQ_LENS = {
     2: "U[512,4096]",
@@ -56,29 +66,96 @@ def kernel_source_digest() -> str:
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
+        path = os.path.join(CSRC, name)
+        if not os.path.isfile(path):
+            continue
+        with open(path, "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: int, kv_dtype: str):
-    """HBM bytes per pa_decode call from the committed rocprofv3 counter
-    summary, or None when the summary is missing, is for another workload, or
-    was taken on different kernel sources."""
-    if workload != 3 or kv_dtype != "bf16" or not os.path.exists(PMC_SUMMARY):
-        return None
+def _summary_fields(path):
     fields = {}
-    with open(PMC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].split(": ", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    return fields
+
+
+def measured_traffic(workload_name: str, call: str):
+    """HBM bytes per attention call from the committed rocprofv3 counter
+    summary of this workload and call (``profiles/*_hbm_counters.md``), or
+    None when there is none or it was taken on different kernel sources."""
+    if not os.path.isdir(PROFILES):
         return None
+    digest = kernel_source_digest()
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith("_hbm_counters.md"):
+            continue
+        fields = _summary_fields(os.path.join(PROFILES, name))
+        if fields.get("workload") != workload_name or fields.get("call") != call:
+            continue
+        if fields.get("kernel_source_sha256") != digest:
+            return None
+        try:
+            return int(fields["traffic_bytes_per_call"])
+        except (KeyError, ValueError):
+            return None
+    return None
+
+
+def read_ceiling(dev, reps=5):
+    """GB/s of the random-tile read probe (libpa_probe.so): a permutation of
+    the 4 KiB tiles of a 4 GiB pool, 2,048 waves, non-temporal 16-byte loads.
+    Returns (median GB/s, description) or (None, reason)."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        return None, "libpa_probe.so not built"
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.pa_probe_read_tiles
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    n_tiles = CEILING_POOL_BYTES // CEILING_TILE_BYTES
+    waves = 2048
+    pool = torch.empty(CEILING_POOL_BYTES, dtype=torch.uint8, device=dev)
+    ids = torch.randperm(n_tiles, dtype=torch.int32, device=dev,
+                         generator=torch.Generator(device=dev).manual_seed(7))
+    sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rates = []
+    for k in range(reps + 1):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = fn(pool.data_ptr(), CEILING_POOL_BYTES, ids.data_ptr(), n_tiles, CEILING_TILE_BYTES,
+                sink.data_ptr(), waves, ctypes.c_void_p(stream.cuda_stream))
+        b.record(stream)
+        if rc != 0:
+            return None, f"probe returned {rc}"
+        torch.cuda.synchronize()
+        if k > 0:
+            rates.append(CEILING_POOL_BYTES / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del pool, ids, sink
+    torch.cuda.empty_cache()
+    return percentile(rates, 50), (f"random {CEILING_TILE_BYTES // 1024} KiB tiles of a "
+                                   f"{CEILING_POOL_BYTES >> 30} GiB pool, {waves} waves, "
+                                   f"non-temporal 16-byte loads; median of {reps} reads")
+
+
+def cpu_model() -> str:
     try:
-        return int(fields["traffic_bytes_per_call"])
-    except (KeyError, ValueError):
-        return None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
@@ -96,10 +173,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget for the oracle baseline")
-    p.add_argument("--flush", action="store_true",
+    p.add_argument("--flush", action=argparse.BooleanOptionalAction, default=True,
                    help="write a 1 GiB scratch buffer before every step, outside the timed "
                         "events, so that no step reads K/V left in the 256 MB Infinity Cache "
-                        "by the step before; ms_per_step is then the mean of per-step events")
+                        "by the step before; ms_per_step is then the mean of per-step events "
+                        "(default on; --no-flush times back-to-back steps)")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the random-tile read probe (the roofline's second denominator)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="also run one plain device copy of BYTES bytes (a reference for "
                         "hardware byte counters)")
@@ -163,6 +243,12 @@ def cpu_baseline(wl, budget_s, kv_dtype):
                  t["v_scales"].cpu())
     else:
         pools = (t["k_cache"].cpu(), t["v_cache"].cpu())
+    affinity = len(os.sched_getaffinity(0))
+    threads = affinity
+    env_threads = os.environ.get("OMP_NUM_THREADS", "")
+    if env_threads.isdigit() and int(env_threads) > 0:
+        threads = min(threads, int(env_threads))   # the process's CPU share on a shared host
+    torch.set_num_threads(threads)
     n_seqs = n_rows = n_tok = kv_bytes = 0
     per_tok = kv_bytes_per_token(wl.shape, kv_dtype)
     t0 = time.perf_counter()
@@ -182,6 +268,8 @@ def cpu_baseline(wl, budget_s, kv_dtype):
         "unit": "tokens/s",
         "kv_gbs": round(kv_bytes / dt / 1e9, 4),
         "cores": torch.get_num_threads(),
+        "affinity_cpus": affinity,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{n_seqs} sequences of the same batch (cycled; {n_rows} query rows, {n_tok} "
                   f"cached tokens, all {wl.shape.num_q_heads} heads each) in {dt:.1f} s",
@@ -271,12 +359,14 @@ def main():
 
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
 
-    def step(ev=None, sev=None):
+    def step(ev=None, sev=None, wev=None):
         if scratch is not None:
             scratch.fill_(1)  # evicts the Infinity Cache; outside every timed event
         if sev is not None:
             sev[0].record(stream)
         binding.compute_slot_mapping(bt, lens, qsl, shp.block_size, num_tokens=T, out=slots)
+        if wev is not None:
+            wev.record(stream)
         if fp8:
             binding.reshape_and_cache_fp8(t["key"], t["value"], t["k_cache8"], t["v_cache8"],
                                           t["k_scales"], t["v_scales"], slots)
@@ -306,11 +396,12 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)] if args.flush else [None] * args.steps
+            for _ in range(args.steps)]
+    wevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        step(evs[k], sevs[k])
+        step(evs[k], sevs[k], wevs[k])
     stop.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
@@ -319,6 +410,8 @@ def main():
         ms_step = sum(a.elapsed_time(b) for a, b in sevs) / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = sum(attn_ms) / len(attn_ms)
+    slot_ms = [a[0].elapsed_time(w) for a, w in zip(sevs, wevs)]
+    write_ms = [w.elapsed_time(e[0]) for w, e in zip(wevs, evs)]
     call = "pa_chunked_prefill" if chunked else ("pa_decode_fp8" if fp8 else "pa_decode")
     if args.shared_prefix:
         call = "pa_decode_shared_prefix"
@@ -327,8 +420,18 @@ def main():
           f"{percentile(attn_ms, 50):.4f}, p90 {percentile(attn_ms, 90):.4f})",
           file=sys.stderr, flush=True)
 
+    # cache write: K and V rows read from the step's tensors and written to
+    # their slots (the fp8 write reads bf16 and writes one byte per element)
+    e_in = 2 if shp.dtype == "bf16" else 4
+    e_out = 1 if fp8 else e_in
+    write_bytes = 2 * T * shp.num_kv_heads * shp.head_dim * (e_in + e_out) + 8 * T
+    ceiling, ceiling_how = (None, "skipped") if args.no_ceiling else read_ceiling(dev)
+    if ceiling is not None:
+        print(f"[bench] read ceiling {ceiling:.1f} GB/s ({ceiling_how})", file=sys.stderr,
+              flush=True)
     kv_bytes, call_bytes = algorithmic_bytes(wl, args.kv_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    workload_name = shp.name if not fp8 else shp.name.replace("-bf16", "-fp8kv")
     if chunked:
         f_chunk, f_single = algorithmic_flops(wl)
         achieved = (f_chunk + f_single) / (attn_avg * 1e-3) / 1e12
@@ -356,8 +459,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "bytes_per_launch": call_bytes,
             "avg_launch_ms": round(attn_avg, 5),
-            "traffic": None if args.shared_prefix else measured_traffic(args.workload,
-                                                                        args.kv_dtype),
+            "traffic": measured_traffic(workload_name, call),
+            "ceiling": None if ceiling is None else {
+                "what": ceiling_how,
+                "achieved_over_ceiling": round(achieved / ceiling, 4),
+                "gbs": round(ceiling, 1),
+            },
         }
     roofline["p10_ms"] = round(percentile(attn_ms, 10), 5)
     roofline["median_ms"] = round(percentile(attn_ms, 50), 5)
@@ -376,7 +483,7 @@ def main():
         "dtype": "fp8-e4m3 cache, bf16 q/out" if fp8 else shp.dtype,
         "data": "synthetic",
         "config": {
-            "workload": shp.name if not fp8 else shp.name.replace("-bf16", "-fp8kv"),
+            "workload": workload_name,
             "num_seqs": wl.num_seqs,
             "num_query_tokens": T,
             "num_q_heads": shp.num_q_heads,
@@ -396,6 +503,13 @@ def main():
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "cache_write": {
+            "call": "pa_reshape_and_cache_fp8" if fp8 else "pa_reshape_and_cache",
+            "avg_us": round(1e3 * sum(write_ms) / len(write_ms), 2),
+            "median_us": round(1e3 * percentile(write_ms, 50), 2),
+            "bytes": write_bytes,
+            "slot_mapping_avg_us": round(1e3 * sum(slot_ms) / len(slot_ms), 2),
+        },
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)

@@ -47,5 +47,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SOURCE = os.path.join(CSRC, "probe", "pa_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile libpa_probe.so, the read-ceiling probe bench.py times beside
+    the attention call (not part of libpa's ABI).  Always recompiles."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC", "-Wall",
+           *DEVICE_FLAGS, PROBE_SOURCE, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
