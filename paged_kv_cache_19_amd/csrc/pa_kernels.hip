@@ -325,6 +325,9 @@ struct KVFrag {
 // within this many powers of two of the running maximum: the exponentials
 // are then at most 2^8 and the final o / l is unchanged.
 constexpr float kLazyRescaleLog2 = 8.f;
+// The chunk kernel's form of it: a lane's 16 probabilities of one step may
+// sum to at most 2^8 before the rows are rescaled (each is then <= 2^8).
+constexpr float kLazyRescaleSum = 256.f;
 
 // Keeps the (rarely taken) rescale branch a branch: without it the compiler
 // turns the block into selects and multiplies the whole accumulator on
@@ -1635,9 +1638,15 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
       // step.
       //
       // Within a step, the S^T of step i+1 is computed between the (masked)
-      // scores of step i and its softmax and PV; the maxima of step i+1 are
-      // taken at the end of step i, while its PV MFMAs run, and the (rare)
-      // rescale of the accumulators happens at the top of step i+1.
+      // scores of step i and its softmax and PV.  The running maximum m is
+      // the true maximum of the piece's first step, then raised only when a
+      // step's probabilities grow too large: p = exp2(s * scale_log2 - m)
+      // is computed with the current m, and when a lane's sum of its 16 p
+      // exceeds 2^8 (or is not finite) the wave takes the rare path, which
+      // raises m of those rows to their true maximum, rescales o and l and
+      // recomputes the step's p.  Every kept p is then at most 2^8, m is at
+      // most the rows' running maximum (so each row with a visible key has a
+      // p >= 1), and no per-step maximum is needed.
       int st_load = 0;  // stage of the next load
       auto load_step = [&](int p) {
         dma(k_begin + 32 * min(p, nsteps - 1), st_load);
@@ -1646,8 +1655,7 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
 #pragma unroll
       for (int p = 0; p <= GS; ++p) load_step(p);
       f32x16 cur[H];
-      float mxn[H];
-      bool grow = false;  // some row's maximum rose by more than kLazyRescaleLog2
+      float nm[H];        // -m, or 0 while the row has seen no key
       int st_cur = 0;     // stage of step i
       for (int g0 = 0; g0 < nsteps; g0 += GS) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1658,9 +1666,13 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
         if (g0 == 0) {
           scores(0, cur);
           if (k_begin + 32 > kv_wmin) mask_scores(cur, k_begin);
-          row_max(cur, mxn);
+          float mx[H];
+          row_max(cur, mx);
 #pragma unroll
-          for (int hf = 0; hf < H; ++hf) m[hf] = mxn[hf];
+          for (int hf = 0; hf < H; ++hf) {
+            m[hf] = mx[hf];
+            nm[hf] = (m[hf] == neg_inf()) ? 0.f : -m[hf];
+          }
         }
 #pragma unroll
         for (int ii = 0; ii < GS; ++ii) {
@@ -1668,34 +1680,52 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
           if (i >= nsteps) break;
           const int st_next = st_cur + 1 == NS ? 0 : st_cur + 1;
           const int c = k_begin + 32 * i;
-          if (grow) {
-            rare_branch();
-#pragma unroll
-            for (int hf = 0; hf < H; ++hf) {
-              const float mnew = fmaxf(m[hf], mxn[hf]);
-              const float alpha = fast_exp2(m[hf] - ((mnew == neg_inf()) ? 0.f : mnew));
-              l[hf] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[hf][dt][r] *= alpha;
-              m[hf] = mnew;
-            }
-          }
           f32x16 nxt[H];
           scores(st_next, nxt);
+          // probabilities of step i (bf16 for the PV MFMA) and their lane sums
+          float ps[H];
           bf16x8 pf[H][2];
-#pragma unroll
-          for (int hf = 0; hf < H; ++hf) {
-            const float nm = (m[hf] == neg_inf()) ? 0.f : -m[hf];
-            float ps = 0.f;
+          auto softmax = [&](int hf) {
+            float t = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float p = fast_exp2(fmaf(cur[hf][r], sl2, nm));
-              ps += p;
+              const float p = fast_exp2(fmaf(cur[hf][r], sl2, nm[hf]));
+              t += p;
               pf[hf][r >> 3][r & 7] = static_cast<__bf16>(p);
             }
-            auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+            ps[hf] = t;
+          };
+          bool over = false;
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf) {
+            softmax(hf);
+            over = over || !(ps[hf] <= kLazyRescaleSum);
+          }
+          if (__builtin_amdgcn_ballot_w64(over) != 0) {
+            // some row's probabilities grew past 2^8: raise its m to its
+            // true maximum so far, rescale, recompute this step's p
+            rare_branch();
+            float mx[H];
+            row_max(cur, mx);
+#pragma unroll
+            for (int hf = 0; hf < H; ++hf) {
+              const float mnew = fmaxf(m[hf], mx[hf]);
+              if (mnew > m[hf]) {
+                const float alpha = fast_exp2(m[hf] - mnew);   // 0 when m was -inf
+                l[hf] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                  for (int r = 0; r < 16; ++r) o[hf][dt][r] *= alpha;
+                m[hf] = mnew;
+                nm[hf] = -mnew;
+              }
+              softmax(hf);
+            }
+          }
+#pragma unroll
+          for (int hf = 0; hf < H; ++hf) {
+            auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps[hf]), __float_as_uint(ps[hf]), false, false);
             l[hf] += __uint_as_float(q[0]) + __uint_as_float(q[1]);
           }
           const uint16_t* vt = smem[st_cur][1];
@@ -1731,13 +1761,8 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
 #pragma unroll
               for (int hf = 0; hf < H; ++hf)
                 o[hf][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][k2], pf[hf][k2], o[hf][dt], 0, 0, 0);
-          // next step's scores: mask, maxima, rescale decision
+          // next step's scores: keys past a row's limit get -inf
           if (c + 64 > kv_wmin) mask_scores(nxt, c + 32);
-          row_max(nxt, mxn);
-          bool g = false;
-#pragma unroll
-          for (int hf = 0; hf < H; ++hf) g = g || mxn[hf] > m[hf] + kLazyRescaleLog2;
-          grow = __builtin_amdgcn_ballot_w64(g) != 0;
 #pragma unroll
           for (int hf = 0; hf < H; ++hf) cur[hf] = nxt[hf];
           st_cur = st_next;

@@ -112,6 +112,22 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("qscale", [4.0, 16.0])
+def test_chunk_rows_rescale_on_large_logits(qscale):
+    """Queries scaled up (by a power of two, exact in bf16) spread the scores
+    so that a row's maximum keeps rising over its keys: the chunk kernel's
+    rescale of o and l (taken when a step's probabilities grow past 2^8)
+    runs many times per row and must still match the oracle."""
+    shape = workloads.Shape("big-logits", workloads.BF16, 8, 2, 128, 16)
+    wl = workloads.make_workload(2, seed=97, device="cuda", seq_lens=[3000, 1200, 700, 90],
+                                 q_lens=[400, 300, 1, 90], shape=shape)
+    wl.tensors["query"].mul_(qscale)
+    log(f"[rescale] query x {qscale}")
+    out, err = run_and_compare(wl, force_chunked=True)
+    log(f"[rescale] max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("case", EDGE, ids=[f"edge{i}" for i in range(len(EDGE))])
 def test_edge_shapes(case):
     dtype, Hq, Hkv, D, B, lens, qls = case
