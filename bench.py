@@ -289,9 +289,8 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     fp8 = args.kv_dtype == "fp8"
-    if fp8 and (args.workload == 5 or args.kv_split):
-        print("the fp8 cache runs the balanced decode only (no chunked prefill, no fixed "
-              "split)", file=sys.stderr)
+    if fp8 and args.kv_split:
+        print("the fp8 cache runs the balanced decode only (no fixed split)", file=sys.stderr)
         sys.exit(2)
 
     if args.shared_prefix and (args.workload == 5 or args.kv_split):
@@ -323,6 +322,10 @@ def main():
     if args.shared_prefix:
         ws_bytes = binding.decode_shared_prefix_workspace_bytes(S, Hq, D, wl.max_seq_len,
                                                                 shp.block_size, prefix_blocks)
+    elif chunked and fp8:
+        cap = binding.chunk_context_blocks(wl.seq_lens, wl.query_start_loc(), shp.block_size)
+        ws_bytes = binding.chunked_prefill_fp8_workspace_bytes(
+            S, T, Hq, shp.num_kv_heads, D, wl.max_seq_len, bt.shape[1], shp.block_size, cap)
     elif chunked:
         ws_bytes = binding.chunked_prefill_workspace_bytes(S, T, Hq, D, wl.max_seq_len,
                                                            shp.block_size, args.kv_split)
@@ -343,6 +346,11 @@ def main():
             binding.decode_shared_prefix(t["query"], kc, vc, bt, lens, wl.max_seq_len, wl.scale,
                                          prefix_blocks, block_refcounts=refcounts, out=out,
                                          workspace=ws, **scales)
+        elif chunked and fp8:
+            binding.chunked_prefill_fp8(t["query"], t["k_cache8"], t["v_cache8"], t["k_scales"],
+                                        t["v_scales"], bt, lens, qsl, wl.max_seq_len,
+                                        wl.max_query_len, wl.scale, cap,
+                                        block_refcounts=refcounts, out=out, workspace=ws)
         elif chunked:
             binding.chunked_prefill(t["query"], t["k_cache"], t["v_cache"], bt, lens, qsl,
                                     wl.max_seq_len, wl.max_query_len, wl.scale,
@@ -412,7 +420,8 @@ def main():
     attn_avg = sum(attn_ms) / len(attn_ms)
     slot_ms = [a[0].elapsed_time(w) for a, w in zip(sevs, wevs)]
     write_ms = [w.elapsed_time(e[0]) for w, e in zip(wevs, evs)]
-    call = "pa_chunked_prefill" if chunked else ("pa_decode_fp8" if fp8 else "pa_decode")
+    call = ("pa_chunked_prefill" + ("_fp8" if fp8 else "")) if chunked else (
+        "pa_decode_fp8" if fp8 else "pa_decode")
     if args.shared_prefix:
         call = "pa_decode_shared_prefix"
     print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, {call} avg "
@@ -436,9 +445,12 @@ def main():
         f_chunk, f_single = algorithmic_flops(wl)
         achieved = (f_chunk + f_single) / (attn_avg * 1e-3) / 1e12
         roofline = {
-            "kernel": "pa_chunked_prefill: one persistent launch splitting the CUs between the "
-                      "query-chunk units (MFMA) and the balanced decode of the single-token "
-                      "rows, then the merges",
+            "kernel": ("pa_chunked_prefill_fp8: the query-chunk sequences' blocks staged as "
+                       "bf16, the chunk kernel (MFMA) on them, the e4m3 balanced decode of the "
+                       "single-token rows, then the merges") if fp8 else
+                      ("pa_chunked_prefill: one persistent launch splitting the CUs between "
+                       "the query-chunk units (MFMA) and the balanced decode of the "
+                       "single-token rows, then the merges"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -325,6 +325,49 @@ int pa_decode_fp8(void* out, const void* query, const void* k_cache,
                   int32_t num_blocks, float scale, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * Workspace for pa_chunked_prefill_fp8: that of pa_chunked_prefill plus the
+ * bf16 staging pools of the query-chunk sequences (chunk_context_blocks
+ * blocks, K and V) and their staging tables.  0 for invalid arguments.
+ */
+size_t pa_chunked_prefill_fp8_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_seq_len,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              int64_t chunk_context_blocks);
+
+/*
+ * pa_chunked_prefill_fp8 -- pa_chunked_prefill against e4m3 pools (the
+ * serving configuration that pairs an fp8 KV cache with chunked prefill:
+ * "Tech Radar ...", section "5.2 Production Python 3.12+ Dynamic Chunked
+ * Prefill Controller", the serving config; the cache format as for
+ * pa_decode_fp8).  bf16 query [num_tokens, num_q_heads, head_dim] and out;
+ * every row computes the attention pa_chunked_prefill defines over the
+ * dequantised values value(code) * scale.
+ * Work: the blocks of every sequence with more than one query row are first
+ * staged in the workspace as bf16 (value(code) * scale rounded to nearest
+ * even, one rounding more than the e4m3 decode makes) and the bf16 chunk
+ * kernel runs on them; single-token rows run the e4m3 balanced decode on the
+ * pools themselves.
+ * chunk_context_blocks: room in the staging pools, at least the sum over
+ * sequences with q_len > 1 of ceil(seq_len / block_size) (the batch builder
+ * knows it); >= 1 when max_query_len > 1, else PA_ERR_SHAPE.  A batch that
+ * needs more is PA_ERR_INDEX under PA_CHECK=1; without it, the blocks past
+ * the room are not staged and those rows are undefined (every access stays
+ * inside the pools).  block_size 16, 32 or 64; at most 2048 sequences.
+ * Other arguments, errors and the workspace ownership as for
+ * pa_chunked_prefill and pa_decode_fp8.
+ */
+int pa_chunked_prefill_fp8(void* out, const void* query, const void* k_cache,
+                           const void* v_cache, const float* k_scales, const float* v_scales,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* block_refcounts, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_seq_len, int32_t max_query_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int64_t chunk_context_blocks, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace for pa_decode_shared_prefix; 0 for invalid arguments (also
  * when prefix_blocks * block_size > max_seq_len). */
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

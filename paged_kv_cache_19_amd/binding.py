@@ -59,6 +59,11 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
     "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _vp]),
+    "pa_chunked_prefill_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                     _i32, ctypes.c_int64]),
+    "pa_chunked_prefill_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                              _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, ctypes.c_int64, _f32, _vp, _sz, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -431,6 +436,60 @@ def decode_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
         max_seq_len, Hq, Hkv, D, B, NB, scale, _ptr(workspace), workspace.numel(),
         _stream(stream)))
+    return out
+
+
+def chunked_prefill_fp8_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                        head_dim, max_seq_len, max_blocks_per_seq, block_size,
+                                        chunk_context_blocks) -> int:
+    n = lib().pa_chunked_prefill_fp8_workspace_bytes(num_seqs, num_tokens, num_q_heads,
+                                                     num_kv_heads, head_dim, max_seq_len,
+                                                     max_blocks_per_seq, block_size,
+                                                     chunk_context_blocks)
+    if n == 0:
+        raise PAError("pa_chunked_prefill_fp8_workspace_bytes", -2)
+    return n
+
+
+def chunk_context_blocks(seq_lens, query_start_loc, block_size: int) -> int:
+    """Staging blocks pa_chunked_prefill_fp8 needs: the sum of ceil(L / B)
+    over sequences with more than one query row (host lists or tensors)."""
+    lens = [int(x) for x in (seq_lens.tolist() if hasattr(seq_lens, "tolist") else seq_lens)]
+    qsl = [int(x) for x in (query_start_loc.tolist() if hasattr(query_start_loc, "tolist")
+                            else query_start_loc)]
+    return sum(-(-L // block_size) for s, L in enumerate(lens) if qsl[s + 1] - qsl[s] > 1)
+
+
+def chunked_prefill_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        k_scales: torch.Tensor, v_scales: torch.Tensor,
+                        block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                        query_start_loc: torch.Tensor, max_seq_len: int, max_query_len: int,
+                        scale: float, chunk_context_blocks: int,
+                        block_refcounts: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_chunked_prefill over e4m3 pools (query chunks staged as bf16)."""
+    NB, Hkv, B, D = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    if query.dtype != torch.bfloat16:
+        raise ValueError("the fp8 chunked prefill takes a bf16 query")
+    _rows(query, out, Hkv, D)
+    T, Hq = query.shape[0], query.shape[1]
+    S = seq_lens.numel()
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB, query_start_loc)
+    _workspace(workspace)
+    _same_device(query, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                 query_start_loc, block_refcounts, out, workspace)
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(chunked_prefill_fp8_workspace_bytes(
+            S, T, Hq, Hkv, D, max_seq_len, block_tables.shape[1], B, chunk_context_blocks),
+            dtype=torch.uint8, device=query.device)
+    _check("pa_chunked_prefill_fp8", lib().pa_chunked_prefill_fp8(
+        _ptr(out), _ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens),
+        _ptr(query_start_loc), S, T, max_seq_len, max_query_len, Hq, Hkv, D, B, NB,
+        chunk_context_blocks, scale, _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -354,6 +354,47 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// Workspace of pa_chunked_prefill_fp8: the bf16 chunked-prefill plan, then
+// the staging offsets (int32 [S + 1]), the staging tables (int32 [S,
+// max_blocks]) and the bf16 staging pools (K then V, cap blocks each).
+struct Fp8ChunkPlan {
+  WorkspacePlan base;
+  size_t off = 0, tables = 0, pool_k = 0, pool_v = 0, total = 0;
+};
+
+bool plan_chunked_fp8(int num_seqs, int num_tokens, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_seq_len, int max_blocks, int block_size,
+                      int64_t cap_blocks, Fp8ChunkPlan* p) {
+  if (num_kv_heads <= 0 || max_blocks <= 0 || cap_blocks < 0) return false;
+  if (!plan_workspace(num_tokens, num_seqs, num_q_heads, head_dim, max_seq_len, block_size, 0,
+                      true, &p->base))
+    return false;
+  const size_t pool = (size_t)cap_blocks * num_kv_heads * block_size * head_dim * 2;
+  p->off = p->base.total;
+  p->tables = p->off + align_up((size_t)(num_seqs + 1) * 4);
+  p->pool_k = p->tables + align_up((size_t)num_seqs * max_blocks * 4);
+  p->pool_v = p->pool_k + align_up(pool);
+  p->total = p->pool_v + align_up(pool);
+  return true;
+}
+
+// PA_CHECK: the staging pool holds every block of the multi-token sequences.
+int validate_stage_capacity(const int32_t* d_lens, const int32_t* d_qsl, int num_seqs,
+                            int block_size, int max_blocks, int64_t cap, hipStream_t st) {
+  std::vector<int32_t> lens(num_seqs), qsl(num_seqs + 1);
+  if (hipMemcpyAsync(lens.data(), d_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipMemcpyAsync(qsl.data(), d_qsl, qsl.size() * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  int64_t need = 0;
+  for (int s = 0; s < num_seqs; ++s)
+    if (qsl[s + 1] - qsl[s] > 1)
+      need += std::min((std::max(lens[s], 0) + block_size - 1) / block_size, max_blocks);
+  return need <= cap ? PA_OK : PA_ERR_INDEX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -673,6 +714,123 @@ int pa_decode_fp8(void* out, const void* query, const void* k_cache, const void*
                           block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                           PA_BF16, 0, workspace, workspace_bytes, stream, f8);
+}
+
+size_t pa_chunked_prefill_fp8_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_seq_len,
+                                              int32_t max_blocks_per_seq, int32_t block_size,
+                                              int64_t chunk_context_blocks) {
+  if (block_size < 16) return 0;
+  Fp8ChunkPlan p;
+  if (!plan_chunked_fp8(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                        max_blocks_per_seq, block_size, chunk_context_blocks, &p))
+    return 0;
+  return p.total;
+}
+
+int pa_chunked_prefill_fp8(void* out, const void* query, const void* k_cache,
+                           const void* v_cache, const float* k_scales, const float* v_scales,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* block_refcounts, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                           int32_t max_seq_len, int32_t max_query_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int64_t chunk_context_blocks, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, PA_BF16);
+  if (rc != PA_OK) return rc;
+  if (block_size < 16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      max_seq_len <= 0 || max_query_len <= 0 || chunk_context_blocks < 0 || !isfinite(scale) ||
+      !(scale > 0.f))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !k_scales || !v_scales || !block_tables ||
+      !seq_lens || !query_start_loc)
+    return PA_ERR_NULL;
+  if (num_seqs > pa::kMaxChunkSeqs) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * num_kv_heads > 65535 || (int64_t)num_tokens > 65535 * 64)
+    return PA_ERR_UNSUPPORTED;
+  if (chunk_context_blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  // query chunks need a staging pool of at least one block (every staging
+  // table entry is clamped into it)
+  if (max_query_len > 1 && chunk_context_blocks < 1) return PA_ERR_SHAPE;
+  Fp8ChunkPlan plan;
+  if (!plan_chunked_fp8(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                        max_blocks_per_seq, block_size, chunk_context_blocks, &plan))
+    return PA_ERR_SHAPE;
+  if (plan.base.max_splits > 65535) return PA_ERR_UNSUPPORTED;
+  if (!workspace) return PA_ERR_WORKSPACE;
+  if (workspace_bytes < plan.total) return PA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (check_enabled()) {
+    rc = validate_metadata(block_tables, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                           num_tokens, max_seq_len, max_query_len, block_size, num_blocks, st);
+    if (rc != PA_OK) return rc;
+    std::vector<int64_t> used;
+    rc = table_blocks_used(block_tables, max_blocks_per_seq, seq_lens, num_seqs, block_size, st,
+                           &used);
+    if (rc == PA_OK)
+      rc = validate_scales(k_scales, v_scales, num_blocks, num_kv_heads, used, st);
+    if (rc == PA_OK)
+      rc = validate_stage_capacity(seq_lens, query_start_loc, num_seqs, block_size,
+                                   max_blocks_per_seq, chunk_context_blocks, st);
+    if (rc != PA_OK) return rc;
+  }
+  const WorkspacePlan& wp = plan.base;
+  char* ws = static_cast<char*>(workspace);
+  pa::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.bf16 = 1;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.q = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.block_refcounts = block_refcounts;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.out = out;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + wp.a_o);
+  a.row_pieces = reinterpret_cast<int32_t*>(ws + wp.a_o + wp.a_ml);
+  char* wb = ws + wp.rp;  // region B and the header follow the piece counts
+  a.sk_part_o = reinterpret_cast<float*>(wb + wp.a_o + wp.a_ml);
+  a.sk_part_ml = reinterpret_cast<float*>(wb + wp.a_o + wp.a_ml + wp.b_o);
+  a.sk_slots = wp.max_pieces;
+  void* header = wb + wp.a_o + wp.a_ml + wp.b_o + wp.b_ml;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.log2_block = log2i(block_size);
+  a.num_blocks = num_blocks;
+  a.split_tokens = wp.split_tokens;
+  a.max_splits = wp.max_splits;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.chunk_steps = wp.chunk_steps;
+  a.chunk_auto = wp.chunk_auto;
+  a.kv_fp8 = 1;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  // the same call on the bf16 staging pools, for the chunk kernel
+  pa::AttnArgs c = a;
+  c.kv_fp8 = 0;
+  c.k_scales = nullptr;
+  c.v_scales = nullptr;
+  c.block_refcounts = nullptr;  // staging blocks are private
+  c.k_cache = ws + plan.pool_k;
+  c.v_cache = ws + plan.pool_v;
+  c.block_tables = reinterpret_cast<const int32_t*>(ws + plan.tables);
+  c.num_blocks = (int32_t)std::max<int64_t>(chunk_context_blocks, 1);
+  return pa::launch_chunked_fp8(a, c, header, chunk_context_blocks,
+                                reinterpret_cast<int32_t*>(ws + plan.off), st) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -113,6 +113,18 @@ constexpr int kMaxMixSeqs = 1024;
 // (16 + 4 * (num_seqs + 1) bytes); a.max_splits is the piece capacity per row.
 hipError_t launch_decode_streamk(const AttnArgs& a, void* header, hipStream_t stream);
 
+// Query chunks and single-token rows over an e4m3 cache.  ``dec`` describes
+// the call on the e4m3 pools (kv_fp8 = 1, the caller's tables); ``chunk`` is
+// the same call on the bf16 staging pools (k_cache / v_cache: room for
+// cap_blocks blocks in the bf16 layouts; block_tables: [num_seqs,
+// max_blocks] int32 staging tables, written here; kv_fp8 = 0).  The blocks
+// of every multi-token sequence are staged as bf16, the chunk kernel runs
+// on the staging pools, the balanced e4m3 decode on the single-token rows,
+// then the merge of cut chunk rows.  ``offsets`` is int32 [num_seqs + 1]
+// workspace.
+hipError_t launch_chunked_fp8(const AttnArgs& dec, const AttnArgs& chunk, void* header,
+                              int64_t cap_blocks, int32_t* offsets, hipStream_t stream);
+
 // True when the MFMA kernels serve this shape (bf16, B >= 8, D in {64,128}).
 bool mfma_path(const AttnArgs& a);
 

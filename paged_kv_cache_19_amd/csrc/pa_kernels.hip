@@ -1849,16 +1849,17 @@ void prefill_kernel(AttnArgs a, int num_wgs) {
 // workgroups run prefill_ranges; each wave of a decode workgroup is one wave
 // of the balanced decode (two fragment sets, so that both kinds fit the same
 // 256-register budget).
-// Relative CU-time per step (D = 128; half at D = 64), in ns of one CU.
-// Both are the values at which the chunked-prefill mix (4 x 512-token chunks
-// + 60 decode rows) ran fastest in steady state (after the clocks have
-// ramped up): decode swept over 410..2000 with the chunk cost at 1490, then
-// the chunk cost over 1100..2400 (64 of 256 workgroups on the decode rows;
-// 56 and 72 were 10% and 3.5% slower).  The decode step is worth more than
-// its bytes at the HBM rate: a CU streams far below its share of HBM
-// bandwidth.
-constexpr int64_t kChunkStepNs = 1750;
-constexpr int64_t kDecodeStepNs = 700;
+// Relative CU-time per step (D = 128; half at D = 64), in ns of one CU,
+// each measured on a batch of one kind only, with every CU on it: 4 query
+// chunks of 512 tokens over 1-8K context (45,056 chunk steps in 291 us on
+// 256 CUs -> 1,650 ns) and 60 decode rows of 256-4,096 keys through the
+// same launch (35,744 decode steps in 107 us -> 770 ns).  The decode step
+// costs a CU more than its bytes at the HBM rate: one CU streams far below
+// its share of HBM bandwidth.  On four mixes (4 x 512 chunks + 60 decode
+// rows, 1 x 2,048 + 200, 8 x 512 + 8, 2 x 256 + 120) the split these give
+// is within 1.5-3% of the best split found by sweeping it.
+constexpr int64_t kChunkStepNs = 1650;
+constexpr int64_t kDecodeStepNs = 770;
 
 template <int D>
 __global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
@@ -2247,7 +2248,135 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   return a.max_splits > 1 ? launch_merge<ES, D>(a, 0, st) : hipSuccess;
 }
 
+// ---------------------------------------------------------------------------
+// Query chunks over an e4m3 cache.  Chunked prefill is bound by the matrix
+// cores and the chunk kernel by its vector work per score, so widening codes
+// inside it would cost more than one pass over the context: the blocks of
+// every multi-token sequence are first staged as bf16 (value(code) * scale,
+// rounded to nearest even) into a staging pool, and the bf16 chunk kernel
+// runs on that pool.  Single-token rows read the e4m3 pools directly through
+// the e4m3 balanced decode.
+// ---------------------------------------------------------------------------
+
+// Staged blocks of sequence s: nblk(s) = its table blocks when it has more
+// than one query row, else 0.  off[s] = sum of nblk over sequences before s,
+// off[S] = the total.  One workgroup of 256 threads.
+__global__ __launch_bounds__(256) void stage_offsets_kernel(AttnArgs a, int32_t* __restrict__ off) {
+  __shared__ int part[256];
+  const int S = a.num_seqs;
+  const int tid = threadIdx.x;
+  const int per = (S + 255) / 256;
+  const int lo = min(tid * per, S), hi = min(lo + per, S);
+  auto nblk = [&](int s) {
+    int r0, qn;
+    seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+    return qn > 1 ? table_blocks(a.seq_lens[s], a.log2_block, a.max_blocks) : 0;
+  };
+  int run = 0;
+  for (int s = lo; s < hi; ++s) run += nblk(s);
+  part[tid] = run;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int x = part[t];
+      part[t] = acc;
+      acc += x;
+    }
+    off[S] = acc;
+  }
+  __syncthreads();
+  int acc = part[tid];
+  for (int s = lo; s < hi; ++s) {
+    off[s] = acc;
+    acc += nblk(s);
+  }
+}
+
+// Workgroup (j, s): logical block j of sequence s (a multi-token sequence)
+// into staging block off[s] + j, K and V of every KV head, and the staging
+// table entry.  Table entries past the sequence's blocks repeat its last
+// staging block; a staging block past the pool's capacity is not written
+// and the entry is clamped to the pool (out-of-contract capacities give
+// wrong results, never an access outside the pools).
+template <int D>
+__global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_t* __restrict__ off,
+                                                        int64_t cap, uint16_t* __restrict__ sk,
+                                                        uint16_t* __restrict__ sv,
+                                                        int32_t* __restrict__ stab) {
+  const int j = blockIdx.x;
+  const int s = blockIdx.y;
+  int r0, qn;
+  seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
+  if (qn <= 1) return;
+  const int nblk = table_blocks(a.seq_lens[s], a.log2_block, a.max_blocks);
+  const int64_t base = off[s];
+  if (threadIdx.x == 0) {
+    const int64_t e = min(base + min(j, max(nblk - 1, 0)), max(cap - 1, (int64_t)0));
+    stab[(int64_t)s * a.max_blocks + j] = (int32_t)e;
+  }
+  if (j >= nblk || base + j >= cap) return;
+  const int64_t dst = base + j;
+  const int phys = clampi(a.block_tables[(int64_t)s * a.max_blocks + j], 0, a.num_blocks - 1);
+  const int Hkv = a.num_kv_heads;
+  const int64_t tile = (int64_t)D << a.log2_block;  // elements of one (block, KV head) tile
+  const int64_t n = Hkv * tile;
+  const uint8_t* k8 = static_cast<const uint8_t*>(a.k_cache) + phys * n;
+  const uint8_t* v8 = static_cast<const uint8_t*>(a.v_cache) + phys * n;
+  uint16_t* k16 = sk + dst * n;
+  uint16_t* v16 = sv + dst * n;
+  for (int64_t e = (int64_t)threadIdx.x * 16; e < n; e += 256 * 16) {
+    const int h = (int)(e / tile);  // 16 elements never straddle a tile (tile % 16 == 0)
+    const float ks = a.k_scales[(int64_t)phys * Hkv + h];
+    const float vs = a.v_scales[(int64_t)phys * Hkv + h];
+#pragma unroll
+    for (int pool = 0; pool < 2; ++pool) {
+      const u32x4 c = *reinterpret_cast<const u32x4*>((pool ? v8 : k8) + e);
+      const float sc = pool ? vs : ks;
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], false);
+        const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], true);
+        w[2 * q] = f32_to_bf16_bits(lo2[0] * sc) | ((uint32_t)f32_to_bf16_bits(lo2[1] * sc) << 16);
+        w[2 * q + 1] = f32_to_bf16_bits(hi2[0] * sc) | ((uint32_t)f32_to_bf16_bits(hi2[1] * sc) << 16);
+      }
+      u32x4* d = reinterpret_cast<u32x4*>((pool ? v16 : k16) + e);
+      d[0] = u32x4{w[0], w[1], w[2], w[3]};
+      d[1] = u32x4{w[4], w[5], w[6], w[7]};
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_chunked_fp8_d(const AttnArgs& dec, const AttnArgs& chunk, void* header,
+                                int64_t cap, int32_t* off, hipStream_t st) {
+  stage_offsets_kernel<<<1, 256, 0, st>>>(dec, off);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (dec.max_query_len > 1) {
+    stage_fp8_kernel<D><<<dim3(dec.max_blocks, dec.num_seqs), 256, 0, st>>>(
+        dec, off, cap, static_cast<uint16_t*>(const_cast<void*>(chunk.k_cache)),
+        static_cast<uint16_t*>(const_cast<void*>(chunk.v_cache)),
+        const_cast<int32_t*>(chunk.block_tables));
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = launch_prefill<D>(chunk, st);
+    if (err != hipSuccess) return err;
+  }
+  err = launch_streamk<D, true>(dec, header, st);
+  if (err != hipSuccess) return err;
+  return chunk.max_splits > 1 ? launch_merge<2, D>(chunk, 1, st) : hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_chunked_fp8(const AttnArgs& dec, const AttnArgs& chunk, void* header,
+                              int64_t cap_blocks, int32_t* offsets, hipStream_t stream) {
+  return dec.head_dim == 128
+             ? launch_chunked_fp8_d<128>(dec, chunk, header, cap_blocks, offsets, stream)
+             : launch_chunked_fp8_d<64>(dec, chunk, header, cap_blocks, offsets, stream);
+}
 
 hipError_t launch_decode_streamk(const AttnArgs& a, void* header, hipStream_t stream) {
   if (a.kv_fp8)

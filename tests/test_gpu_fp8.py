@@ -202,3 +202,101 @@ def test_fp8_pa_check_rejects_bad_scales(monkeypatch):
         binding.reshape_and_cache_fp8(t["key"], t["value"], t["k_cache8"], t["v_cache8"],
                                       t["k_scales"], t["v_scales"], slots)
     assert e.value.status == -6
+
+
+# -- query chunks over the e4m3 cache (pa_chunked_prefill_fp8) --------------------
+
+def _run_fp8_chunked(wl, cap_extra=0):
+    """Slot mapping, the quantising cache write of every query token, then
+    pa_chunked_prefill_fp8; every row against the oracle's attention over
+    the dequantised pools.  Returns (out, max abs err)."""
+    t = wl.tensors
+    dev = wl.device
+    B = wl.shape.block_size
+    _poison_fp8(wl)
+    bt = wl.block_tables_tensor(dev)
+    lens = wl.seq_lens_tensor(dev)
+    qsl = wl.query_start_loc_tensor(dev)
+    slots = binding.compute_slot_mapping(bt, lens, qsl, B, num_tokens=wl.num_tokens)
+    kc0, vc0 = t["k_cache8"].cpu(), t["v_cache8"].cpu()
+    ks, vs = t["k_scales"].cpu(), t["v_scales"].cpu()
+    binding.reshape_and_cache_fp8(t["key"], t["value"], t["k_cache8"], t["v_cache8"],
+                                  t["k_scales"], t["v_scales"], slots)
+    cap = binding.chunk_context_blocks(wl.seq_lens, wl.query_start_loc(), B) + cap_extra
+    out = binding.chunked_prefill_fp8(t["query"], t["k_cache8"], t["v_cache8"], t["k_scales"],
+                                      t["v_scales"], bt, lens, qsl, wl.max_seq_len,
+                                      wl.max_query_len, wl.scale, max(cap, 1),
+                                      block_refcounts=wl.block_refcounts_tensor(dev))
+    torch.cuda.synchronize()
+    slots_ref = ref.compute_slot_mapping(bt.cpu(), wl.seq_lens, wl.query_start_loc(), B)
+    assert torch.equal(slots.cpu(), slots_ref)
+    kq, vq = ref8.reshape_and_cache_fp8(kc0, vc0, ks, vs, t["key"].cpu(), t["value"].cpu(),
+                                        slots_ref)
+    assert torch.equal(t["k_cache8"].cpu(), kq) and torch.equal(t["v_cache8"].cpu(), vq)
+    out_cpu = out.cpu()
+    assert torch.isfinite(out_cpu.float()).all(), "non-finite output (poison reached out?)"
+    expect = ref8.paged_attention_fp8(t["query"].cpu(), kq, vq, ks, vs, bt.cpu(), wl.seq_lens,
+                                      wl.query_start_loc(), wl.scale)
+    return out, (out_cpu.double() - expect).abs().max().item()
+
+
+def test_fp8_chunked_prefill_workload_mix():
+    """Workload 5 (4 x 512-token chunks over 1-8K context + 60 decode rows)
+    on e4m3 pools; every row."""
+    log("[fp8 chunked] workload 5")
+    wl = workloads.make_workload(5, device="cuda", kv_fp8=True)
+    _, err = _run_fp8_chunked(wl)
+    log(f"[fp8 chunked] workload 5: max abs err {err:.3e}")
+    assert err <= TOL
+    del wl
+    torch.cuda.empty_cache()
+
+
+FP8_CHUNK_EDGE = [
+    # Hq, Hkv, D, B, seq_lens, q_lens
+    (32, 8, 128, 16, [600, 17, 9], [600, 5, 1]),            # pure prefill + chunk + decode
+    (8, 2, 128, 16, [40, 2000, 1, 700], [33, 130, 1, 1]),   # ragged chunks
+    (16, 1, 64, 32, [300, 260], [100, 3]),                  # G = 16, D = 64, B = 32
+    (16, 16, 128, 16, [257, 100], [64, 2]),                 # G = 1
+    (8, 2, 128, 64, [700, 130], [300, 64]),                 # B = 64
+    (8, 2, 64, 16, [500, 33], [257, 33]),                   # D = 64
+    (8, 2, 128, 16, [300, 90, 77], [1, 1, 1]),              # decode rows only
+    (8, 2, 128, 32, [3000, 2500], [1000, 700]),             # long chunks, chunks only
+]
+
+
+@pytest.mark.parametrize("case", FP8_CHUNK_EDGE,
+                         ids=[f"fp8-chunk-edge{i}" for i in range(len(FP8_CHUNK_EDGE))])
+def test_fp8_chunked_prefill_edge_cases(case):
+    Hq, Hkv, D, B, lens, qls = case
+    log(f"[fp8 chunked edge] {case}")
+    shape = workloads.Shape("fp8-chunk-edge", workloads.BF16, Hq, Hkv, D, B)
+    wl = workloads.make_workload(2, seed=78, device="cuda", seq_lens=lens, q_lens=qls,
+                                 shape=shape, kv_fp8=True)
+    _, err = _run_fp8_chunked(wl, cap_extra=3)
+    log(f"[fp8 chunked edge] max abs err {err:.3e}")
+    assert err <= TOL
+
+
+def test_fp8_chunked_prefill_checks_its_staging_room(monkeypatch):
+    shape = workloads.Shape("fp8-chunk-room", workloads.BF16, 8, 2, 128, 16)
+    wl = workloads.make_workload(2, seed=79, device="cuda", seq_lens=[300, 40], q_lens=[64, 1],
+                                 shape=shape, kv_fp8=True)
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    lens = wl.seq_lens_tensor("cuda")
+    qsl = wl.query_start_loc_tensor("cuda")
+    need = binding.chunk_context_blocks(wl.seq_lens, wl.query_start_loc(), 16)
+    assert need == 19
+    args = (t["query"], t["k_cache8"], t["v_cache8"], t["k_scales"], t["v_scales"], bt, lens,
+            qsl, wl.max_seq_len, wl.max_query_len, wl.scale)
+    with pytest.raises(binding.PAError) as e:     # chunks with no staging room at all
+        binding.chunked_prefill_fp8(*args, 0, workspace=torch.empty(
+            1 << 24, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == -2
+    monkeypatch.setenv("PA_CHECK", "1")
+    with pytest.raises(binding.PAError) as e:     # one block short
+        binding.chunked_prefill_fp8(*args, need - 1)
+    assert e.value.status == -6
+    binding.chunked_prefill_fp8(*args, need)
+    torch.cuda.synchronize()
