@@ -20,7 +20,11 @@
  *     are shared (reference count + 1) and not prefilled again ("Inside
  *     vLLM ...", section "Zero-Copy Branching and Parallel Sampling");
  *   - preemption by recomputation ("03 -- ...", section "Preemption &
- *     eviction").
+ *     eviction"), or, with a swap space (pa_sched_enable_swap), by swapping:
+ *     the request's blocks are copied to host blocks and released, and later
+ *     copied back into fresh device blocks; the request then continues
+ *     without recomputing ("03 -- ...", same section; "Inside vLLM ...",
+ *     section "Preemption Mechanics: Swapping vs. Recomputation").
  *
  * Readings where the pages are silent: C_avail is consumed in order (running
  * prompt chunks, then admissions); decode tokens are always scheduled; the
@@ -33,7 +37,14 @@
  * the first parent being the FNV offset basis; the preempted request is the
  * one that cannot allocate, its prompt becomes all its tokens, and a step
  * that preempted admits nobody; a request ends when a step computed all its
- * tokens and it has generated max_new_tokens.
+ * tokens and it has generated max_new_tokens.  With a swap space: a
+ * preempted request is swapped out when the swap space has a block for each
+ * of its blocks, else recomputed; host blocks come from a FIFO free list;
+ * swapped-out requests come back in order, in a step that preempted nobody,
+ * after the running requests and before admissions, each while budget is
+ * left and the device has blocks for all its tokens plus the step's (a
+ * decode token takes one unit of budget), and are scheduled in that step;
+ * nobody is admitted while a request is swapped out.
  *
  * All memory here is host memory.  The builder is a plain object owned by the
  * caller (create/destroy); it is not thread-safe.  Nothing here touches the
@@ -102,6 +113,27 @@ int pa_sched_update(pa_sched* s, const int64_t* req_ids, const int32_t* tokens,
 /* Reference count of every block (int32 [num_blocks]): the block_refcounts
  * hint of pa_decode / pa_chunked_prefill. */
 int pa_sched_block_refcounts(const pa_sched* s, int32_t* out, int32_t num_blocks);
+
+/*
+ * Give the builder a swap space of num_host_blocks host blocks (ids 0 ..
+ * num_host_blocks - 1, same block size as the device pool), which makes
+ * swapping the preemption mode whenever the space can take the request.
+ * Call once, before the first request (PA_ERR_INDEX otherwise).
+ */
+int pa_sched_enable_swap(pa_sched* s, int32_t num_host_blocks);
+
+/*
+ * The copies the last step needs, to be run before its cache write and
+ * attention, swap-outs first: swap_out int64 [num_swap_out, 2] (device
+ * block, host block) pairs, swap_in int64 [num_swap_in, 2] (host block,
+ * device block) pairs -- the block_mapping arguments of pa_swap_blocks --
+ * and the ids of the requests swapped out (int64 [num_swapped_out]; they are
+ * also among pa_sched_get_batch's preempted ids).  Call with NULL arrays to
+ * get the counts first.
+ */
+int pa_sched_get_swaps(const pa_sched* s, int32_t* num_swap_out, int32_t* num_swap_in,
+                       int64_t* swap_out, int64_t* swap_in, int64_t* swapped_out_ids,
+                       int32_t* num_swapped_out);
 
 /* Requests waiting, running and finished so far. */
 int pa_sched_counts(const pa_sched* s, int32_t* waiting, int32_t* running,

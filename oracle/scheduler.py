@@ -24,6 +24,11 @@ What the method does, restated from the pages:
 * Preemption by recomputation: the request's blocks are released and it
   returns to the front of the waiting queue, to be prefilled again ("03 --
   ...", section "Preemption & eviction").
+* Preemption by swapping: the request's blocks are copied to host swap
+  space and released on the device; later its blocks are copied back into
+  fresh device blocks and it continues where it stopped, without recomputing
+  ("03 -- ...", section "Preemption & eviction"; "Inside vLLM ...", section
+  "Preemption Mechanics: Swapping vs. Recomputation").
 
 Readings where the pages are silent (each is listed in the design notes):
 
@@ -48,6 +53,21 @@ Readings where the pages are silent (each is listed in the design notes):
   waiting request (memory is short).
 * A request ends when a step computed all its tokens and it has generated
   max_new_tokens; otherwise the caller appends the token it sampled.
+* Swapping (pages name both modes but no rule to choose): with a host swap
+  space of ``num_host_blocks`` blocks, a preempted request is swapped out
+  when the swap space has a host block for each of its device blocks, else
+  recomputed.  Host blocks come from a FIFO free list.  Swapped requests
+  wait in a FIFO of their own; a step that preempted nobody swaps them back
+  in, in order, after the running requests and before any admission, each
+  while budget is left and the device has blocks for all of its tokens plus
+  this step's (a decode token takes one unit of budget here, as its row is
+  not among the step's first reserved decodes).  A swapped-in request gets
+  fresh device blocks, its full blocks are keyed again (unless the keys are
+  taken), and it is scheduled in the same step.  No request is admitted
+  while any is swapped out.  The step reports the copies: swap_out pairs
+  (device block, host block), swap_in pairs (host block, device block); the
+  caller runs the swap-outs before the swap-ins and both before the step's
+  cache write.
 """
 
 from __future__ import annotations
@@ -84,6 +104,7 @@ class Request:
     num_computed: int = 0
     table: List[int] = field(default_factory=list)
     keys: List[int] = field(default_factory=list)   # keys of the table's full blocks
+    host_table: List[int] = field(default_factory=list)  # swap-space blocks while swapped out
 
     @property
     def pending(self) -> int:
@@ -102,7 +123,10 @@ class Scheduled:
 @dataclass
 class Batch:
     entries: List[Scheduled]
-    preempted: List[int]
+    preempted: List[int]                      # every request preempted in this step
+    swapped_out: List[int] = field(default_factory=list)   # those of them swapped out
+    swap_out: List[tuple] = field(default_factory=list)    # (device block, host block)
+    swap_in: List[tuple] = field(default_factory=list)     # (host block, device block)
 
     @property
     def num_tokens(self) -> int:
@@ -117,7 +141,7 @@ class Batch:
 
 class Scheduler:
     def __init__(self, num_blocks: int, block_size: int, token_budget: int, chunk_tokens: int,
-                 free_order: Optional[Sequence[int]] = None):
+                 free_order: Optional[Sequence[int]] = None, num_host_blocks: int = 0):
         self.B = block_size
         self.token_budget = token_budget
         self.chunk_tokens = chunk_tokens
@@ -130,6 +154,9 @@ class Scheduler:
         self.waiting: deque = deque()
         self.running: List[Request] = []
         self.finished: List[int] = []
+        self.num_host_blocks = num_host_blocks
+        self.host_free: deque = deque(range(num_host_blocks))
+        self.swapped: deque = deque()
 
     # -- blocks ----------------------------------------------------------------
     def _allocate(self) -> int:
@@ -186,10 +213,30 @@ class Scheduler:
         self._register_full_blocks(req, req.num_computed)
         return Scheduled(req.req_id, c, req.num_computed, list(req.table), slots)
 
-    def _preempt(self, req: Request) -> None:
+    def _preempt(self, req: Request, swap_out: List[tuple]) -> bool:
+        """Swap the request out when the swap space holds all its blocks,
+        else release them for recomputation.  True when swapped."""
+        if self.num_host_blocks and len(self.host_free) >= len(req.table):
+            for b in req.table:
+                h = self.host_free.popleft()
+                swap_out.append((b, h))
+                req.host_table.append(h)
+            self._release(req)
+            self.swapped.append(req)
+            return True
         self._release(req)
         req.num_computed = 0
         req.prompt_len = len(req.tokens)
+        return False
+
+    def _swap_in(self, req: Request, swap_in: List[tuple]) -> None:
+        for h in req.host_table:
+            b = self._allocate()
+            swap_in.append((h, b))
+            req.table.append(b)
+            self.host_free.append(h)
+        req.host_table = []
+        self._register_full_blocks(req, req.num_computed)
 
     # -- the public steps --------------------------------------------------------
     def add_request(self, req_id: int, prompt: Sequence[int], max_new_tokens: int) -> None:
@@ -200,14 +247,22 @@ class Scheduler:
     def step(self) -> Batch:
         entries: List[Scheduled] = []
         preempted: List[int] = []
+        swapped_out: List[int] = []
+        swap_out: List[tuple] = []
+        swap_in: List[tuple] = []
         decodes = [r for r in self.running if r.num_computed >= r.prompt_len]
         prefills = [r for r in self.running if r.num_computed < r.prompt_len]
         still: List[Request] = []
+
+        def preempt(r):
+            preempted.append(r.req_id)
+            if self._preempt(r, swap_out):
+                swapped_out.append(r.req_id)
+
         # 1. decode streams: one token each, reserved before the budget is split
         for r in decodes:
             if self._blocks_needed(r, 1) > len(self.free):
-                self._preempt(r)
-                preempted.append(r.req_id)
+                preempt(r)
                 continue
             entries.append(self._schedule(r, 1))
             still.append(r)
@@ -219,19 +274,31 @@ class Scheduler:
                 still.append(r)
                 continue
             if self._blocks_needed(r, c) > len(self.free):
-                self._preempt(r)
-                preempted.append(r.req_id)
+                preempt(r)
                 continue
             entries.append(self._schedule(r, c))
             avail -= c
             still.append(r)
-        # preempted requests go back to the front of the queue, in order
-        for rid in reversed(preempted):
+        # requests preempted for recomputation go back to the front of the
+        # queue, in order
+        for rid in reversed([x for x in preempted if x not in swapped_out]):
             req = next(x for x in self.running if x.req_id == rid)
             self.waiting.appendleft(req)
-        # 3. admissions in arrival order while budget is left (none after a
-        #    preemption)
-        while self.waiting and avail > 0 and not preempted:
+        # 3. swapped-out requests come back, in order, when nobody was
+        #    preempted in this step
+        while self.swapped and avail > 0 and not preempted:
+            r = self.swapped[0]
+            c = 1 if r.num_computed >= r.prompt_len else min(r.pending, self.chunk_tokens, avail)
+            if -(-(r.num_computed + c) // self.B) > len(self.free):
+                break
+            self.swapped.popleft()
+            self._swap_in(r, swap_in)
+            entries.append(self._schedule(r, c))
+            avail -= c
+            still.append(r)
+        # 4. admissions in arrival order while budget is left (none after a
+        #    preemption, none while a request is swapped out)
+        while self.waiting and avail > 0 and not preempted and not self.swapped:
             r = self.waiting[0]
             hits = self._lookup(r)
             n_cached = len(hits) * self.B
@@ -252,7 +319,7 @@ class Scheduler:
             avail -= c
             still.append(r)
         self.running = still
-        return Batch(entries, preempted)
+        return Batch(entries, preempted, swapped_out, swap_out, swap_in)
 
     def update(self, batch: Batch, sampled: Dict[int, int]) -> None:
         """After the step ran: requests with every token computed either end
@@ -283,3 +350,9 @@ class Scheduler:
         assert len(self.free) + sum(1 for n in self.rc.values() if n > 0) == len(self.rc)
         for k, b in self.block_of_key.items():
             assert self.key_of_block[b] == k
+        held = [h for r in self.swapped for h in r.host_table]
+        assert len(set(held)) == len(held) and not set(held) & set(self.host_free)
+        assert len(held) + len(self.host_free) == self.num_host_blocks
+        for r in self.swapped:
+            assert not r.table and len(r.host_table) == -(-r.num_computed // self.B)
+            assert r not in self.running

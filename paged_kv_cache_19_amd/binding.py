@@ -52,6 +52,8 @@ SIGNATURES = {
     "pa_sched_update": (ctypes.c_int, [_vp, _vp, _vp, _i32]),
     "pa_sched_block_refcounts": (ctypes.c_int, [_vp, _vp, _i32]),
     "pa_sched_counts": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+    "pa_sched_enable_swap": (ctypes.c_int, [_vp, _i32]),
+    "pa_sched_get_swaps": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pa_reshape_and_cache_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                 _i32, _i32, _i32, _vp]),
     "pa_decode_fp8_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -549,7 +551,7 @@ class BatchBuilder:
     sampled tokens.  Host memory only; arrays are numpy."""
 
     def __init__(self, num_blocks: int, block_size: int, token_budget: int, chunk_tokens: int,
-                 free_order=None):
+                 free_order=None, num_host_blocks: int = 0):
         import numpy as np
         self._np = np
         fo = None
@@ -560,6 +562,8 @@ class BatchBuilder:
                                         None if fo is None else fo.ctypes.data_as(ctypes.c_void_p))
         if not self._h:
             raise PAError("pa_sched_create", -2)
+        if num_host_blocks:
+            _check("pa_sched_enable_swap", lib().pa_sched_enable_swap(self._h, num_host_blocks))
 
     def close(self) -> None:
         if self._h:
@@ -596,6 +600,15 @@ class BatchBuilder:
             self._h, ptr(out["req_ids"]), ptr(out["seq_lens"]), ptr(out["query_start_loc"]),
             ptr(out["block_tables"]), mb, pad_block, ptr(out["slot_mapping"]),
             ptr(out["preempted"]) if P else None))
+        no, ni, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_sched_get_swaps", lib().pa_sched_get_swaps(
+            self._h, ctypes.byref(no), ctypes.byref(ni), None, None, None, ctypes.byref(ns)))
+        out["swap_out"] = np.zeros((no.value, 2), np.int64)
+        out["swap_in"] = np.zeros((ni.value, 2), np.int64)
+        out["swapped_out"] = np.zeros(ns.value, np.int64)
+        _check("pa_sched_get_swaps", lib().pa_sched_get_swaps(
+            self._h, ctypes.byref(no), ctypes.byref(ni), ptr(out["swap_out"]),
+            ptr(out["swap_in"]), ptr(out["swapped_out"]), ctypes.byref(ns)))
         return out
 
     def update(self, sampled: dict) -> None:

@@ -52,6 +52,7 @@ struct Request {
   int32_t prompt_len = 0, max_new = 0, generated = 0, num_computed = 0;
   std::vector<int32_t> table;
   std::vector<uint64_t> keys;  // keys of the table's full blocks
+  std::vector<int32_t> host_table;  // swap-space blocks while swapped out
 };
 
 struct Entry {
@@ -79,6 +80,12 @@ struct pa_sched {
   int32_t finished = 0;
   std::vector<Entry> batch;
   std::vector<int64_t> preempted;
+  // swap space: FIFO of free host blocks; swapped-out requests in order
+  int32_t num_host = 0;
+  std::deque<int32_t> host_free;
+  std::deque<Request*> swapped;
+  std::vector<int64_t> swapped_out;
+  std::vector<std::pair<int32_t, int32_t>> swap_out, swap_in;  // (src, dst) block pairs
 
   void push_back(int32_t b) {
     next[b] = -1;
@@ -146,10 +153,40 @@ struct pa_sched {
     e.table = r->table;
     batch.push_back(std::move(e));
   }
+  // Swap out when the swap space holds all the request's blocks, else
+  // release them for recomputation.
   void preempt(Request* r) {
+    preempted.push_back(r->id);
+    if (num_host > 0 && host_free.size() >= r->table.size()) {
+      for (int32_t b : r->table) {
+        const int32_t h = host_free.front();
+        host_free.pop_front();
+        swap_out.emplace_back(b, h);
+        r->host_table.push_back(h);
+      }
+      release(r);
+      swapped.push_back(r);
+      swapped_out.push_back(r->id);
+      return;
+    }
     release(r);
     r->num_computed = 0;
     r->prompt_len = (int32_t)r->tokens.size();
+  }
+  void swap_back(Request* r) {
+    for (int32_t h : r->host_table) {
+      const int32_t b = allocate();
+      swap_in.emplace_back(h, b);
+      r->table.push_back(b);
+      host_free.push_back(h);
+    }
+    r->host_table.clear();
+    register_full_blocks(r);
+  }
+  bool is_swapped(int64_t id) const {
+    for (int64_t x : swapped_out)
+      if (x == id) return true;
+    return false;
   }
   // Leading full blocks with cached keys: (block, key) pairs.
   void lookup(const Request* r, std::vector<std::pair<int32_t, uint64_t>>* hits) const {
@@ -168,12 +205,14 @@ struct pa_sched {
   void step() {
     batch.clear();
     preempted.clear();
+    swapped_out.clear();
+    swap_out.clear();
+    swap_in.clear();
     std::vector<Request*> decodes, prefills, still;
     for (Request* r : running) (r->num_computed >= r->prompt_len ? decodes : prefills).push_back(r);
     for (Request* r : decodes) {
       if (blocks_needed(r, 1) > free_count) {
         preempt(r);
-        preempted.push_back(r->id);
         continue;
       }
       schedule(r, 1);
@@ -190,16 +229,31 @@ struct pa_sched {
       }
       if (blocks_needed(r, c) > free_count) {
         preempt(r);
-        preempted.push_back(r->id);
         continue;
       }
       schedule(r, c);
       avail -= c;
       still.push_back(r);
     }
-    for (auto it = preempted.rbegin(); it != preempted.rend(); ++it) waiting.push_front(*it);
+    // requests preempted for recomputation go back to the front, in order
+    for (auto it = preempted.rbegin(); it != preempted.rend(); ++it)
+      if (!is_swapped(*it)) waiting.push_front(*it);
+    // swapped-out requests come back, in order, when nobody was preempted
+    while (!swapped.empty() && avail > 0 && preempted.empty()) {
+      Request* r = swapped.front();
+      const int64_t pending = (int64_t)r->tokens.size() - r->num_computed;
+      const int32_t c = r->num_computed >= r->prompt_len
+                            ? 1
+                            : (int32_t)std::min<int64_t>(std::min<int64_t>(pending, chunk), avail);
+      if ((r->num_computed + c + B - 1) / B > free_count) break;
+      swapped.pop_front();
+      swap_back(r);
+      schedule(r, c);
+      avail -= c;
+      still.push_back(r);
+    }
     std::vector<std::pair<int32_t, uint64_t>> hits;
-    while (!waiting.empty() && avail > 0 && preempted.empty()) {
+    while (!waiting.empty() && avail > 0 && preempted.empty() && swapped.empty()) {
       Request* r = reqs[waiting.front()].get();
       lookup(r, &hits);
       const int32_t n_cached = (int32_t)hits.size() * B;
@@ -353,6 +407,37 @@ int pa_sched_block_refcounts(const pa_sched* s, int32_t* out, int32_t num_blocks
   if (!s || !out) return PA_ERR_NULL;
   if (num_blocks != s->nb) return PA_ERR_SHAPE;
   memcpy(out, s->rc.data(), sizeof(int32_t) * (size_t)num_blocks);
+  return PA_OK;
+}
+
+int pa_sched_enable_swap(pa_sched* s, int32_t num_host_blocks) {
+  if (!s) return PA_ERR_NULL;
+  if (num_host_blocks < 0) return PA_ERR_SHAPE;
+  if (!s->reqs.empty() || s->num_host > 0) return PA_ERR_INDEX;  // before any request, once
+  s->num_host = num_host_blocks;
+  for (int32_t h = 0; h < num_host_blocks; ++h) s->host_free.push_back(h);
+  return PA_OK;
+}
+
+int pa_sched_get_swaps(const pa_sched* s, int32_t* num_swap_out, int32_t* num_swap_in,
+                       int64_t* swap_out, int64_t* swap_in, int64_t* swapped_out_ids,
+                       int32_t* num_swapped_out) {
+  if (!s || !num_swap_out || !num_swap_in || !num_swapped_out) return PA_ERR_NULL;
+  *num_swap_out = (int32_t)s->swap_out.size();
+  *num_swap_in = (int32_t)s->swap_in.size();
+  *num_swapped_out = (int32_t)s->swapped_out.size();
+  if (swap_out)
+    for (size_t i = 0; i < s->swap_out.size(); ++i) {
+      swap_out[2 * i] = s->swap_out[i].first;
+      swap_out[2 * i + 1] = s->swap_out[i].second;
+    }
+  if (swap_in)
+    for (size_t i = 0; i < s->swap_in.size(); ++i) {
+      swap_in[2 * i] = s->swap_in[i].first;
+      swap_in[2 * i + 1] = s->swap_in[i].second;
+    }
+  if (swapped_out_ids)
+    for (size_t i = 0; i < s->swapped_out.size(); ++i) swapped_out_ids[i] = s->swapped_out[i];
   return PA_OK;
 }
 

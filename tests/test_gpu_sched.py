@@ -80,3 +80,95 @@ def test_builder_drives_cache_write_and_chunked_prefill():
     assert nat.counts() == (0, 0, 8)
     assert torch.equal(bits(kc_d.cpu()), bits(kc)) and torch.equal(bits(vc_d.cpu()), bits(vc))
 
+
+def test_builder_swaps_preempted_requests_through_pinned_host_pools():
+    """A pool too small for the batch, with a swap space: each step's
+    swap-out and swap-in pairs from the builder run through pa_swap_blocks
+    between the device pools and pinned host pools (swap-outs first), then
+    the cache write and pa_chunked_prefill; every step matches the oracle on
+    CPU mirrors of all four pools, and swapped requests resume without being
+    prefilled again."""
+    import oracle.block_ops as ops
+    B, H, Hq, D, NB, NH, V = 16, 8, 32, 128, 40, 64, 97
+    # the device pool is NB blocks; the steps below run empty ones too (the
+    # builder holds every request back while one is swapped out and cannot
+    # come in yet)
+    g = torch.Generator().manual_seed(23)
+    ktab = torch.randn(V, H, D, generator=g).to(torch.bfloat16)
+    vtab = torch.randn(V, H, D, generator=g).to(torch.bfloat16)
+    qtab = torch.randn(V, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.full((NB, H, B, D), math.nan, dtype=torch.bfloat16)
+    vc = torch.full((NB, H, D, B), math.nan, dtype=torch.bfloat16)
+    kh = torch.full((NH, H, B, D), math.nan, dtype=torch.bfloat16)
+    vh = torch.full((NH, H, D, B), math.nan, dtype=torch.bfloat16)
+    kc_d, vc_d = kc.cuda(), vc.cuda()
+    kh_p, vh_p = kh.clone().pin_memory(), vh.clone().pin_memory()
+    nat = binding.BatchBuilder(NB, B, token_budget=256, chunk_tokens=64, num_host_blocks=NH)
+    rng = random.Random(7)
+    tokens, gen, max_new = {}, {}, {}
+    for rid in range(6):
+        prompt = [rng.randrange(V) for _ in range(rng.randrange(60, 200))]
+        tokens[rid], gen[rid], max_new[rid] = list(prompt), 0, rng.randrange(20, 60)
+        nat.add_request(rid, prompt, max_new_tokens=max_new[rid])
+    scale = D ** -0.5
+    swapped_at, last_len, n_out, n_in, worst = {}, {}, 0, 0, 0.0
+    for step in range(400):
+        b = nat.step()
+        if len(b["swap_out"]):
+            m = torch.from_numpy(b["swap_out"])
+            binding.swap_blocks(kh_p, kc_d, m.cuda())
+            binding.swap_blocks(vh_p, vc_d, m.cuda())
+            kh, vh = ops.copy_blocks(kh, kc, m), ops.copy_blocks(vh, vc, m)
+            n_out += len(b["swapped_out"])
+        if len(b["swap_in"]):
+            m = torch.from_numpy(b["swap_in"])
+            binding.swap_blocks(kc_d, kh_p, m.cuda())
+            binding.swap_blocks(vc_d, vh_p, m.cuda())
+            kc, vc = ops.copy_blocks(kc, kh, m), ops.copy_blocks(vc, vh, m)
+            n_in += 1
+        S = len(b["req_ids"])
+        if S == 0:
+            if nat.counts()[:2] == (0, 0):
+                break
+            continue
+        for rid in b["swapped_out"].tolist():     # stopped with last_len tokens cached
+            swapped_at[rid] = last_len[rid]
+        qsl = b["query_start_loc"].tolist()
+        toks = []
+        for i, rid in enumerate(b["req_ids"].tolist()):
+            L, n = int(b["seq_lens"][i]), qsl[i + 1] - qsl[i]
+            if rid in swapped_at:              # swapped back in: resumes where it stopped
+                assert L - n == swapped_at.pop(rid), (step, rid)
+            last_len[rid] = L
+            toks += tokens[rid][L - n:L]
+        ti = torch.tensor(toks)
+        key, val, q = ktab[ti], vtab[ti], qtab[ti]
+        slots = torch.from_numpy(b["slot_mapping"])
+        bt = torch.from_numpy(b["block_tables"])
+        lens = torch.from_numpy(b["seq_lens"])
+        qsl_t = torch.from_numpy(b["query_start_loc"])
+        binding.reshape_and_cache(key.cuda(), val.cuda(), kc_d, vc_d, slots.cuda())
+        out = binding.chunked_prefill(q.cuda(), kc_d, vc_d, bt.cuda(), lens.cuda(), qsl_t.cuda(),
+                                      int(lens.max()), max(qsl[i + 1] - qsl[i] for i in range(S)),
+                                      scale, block_refcounts=torch.from_numpy(
+                                          nat.block_refcounts()).cuda())
+        torch.cuda.synchronize()
+        kc, vc = ref.reshape_and_cache(kc, vc, key, val, slots)
+        expect = ref.paged_attention(q, kc, vc, bt, lens.tolist(), qsl, scale)
+        err = (out.cpu().double() - expect).abs().max().item()
+        worst = max(worst, err)
+        assert err <= 2e-2, (step, err)
+        sampled = {}
+        for i, rid in enumerate(b["req_ids"].tolist()):
+            if int(b["seq_lens"][i]) == len(tokens[rid]) and gen[rid] < max_new[rid]:
+                sampled[rid] = (rid * 31 + len(tokens[rid]) * 7) % V
+        nat.update(sampled)
+        for rid, t in sampled.items():
+            tokens[rid].append(t)
+            gen[rid] += 1
+    log(f"[builder swap] {step + 1} steps, {n_out} swap-outs, {n_in} swap-ins, "
+        f"worst max abs err {worst:.3e}")
+    assert n_out > 0 and n_in > 0
+    assert nat.counts() == (0, 0, 6)
+    assert torch.equal(bits(kc_d.cpu()), bits(kc)) and torch.equal(bits(vc_d.cpu()), bits(vc))
+    assert torch.equal(bits(kh_p), bits(kh)) and torch.equal(bits(vh_p), bits(vh))

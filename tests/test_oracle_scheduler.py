@@ -21,9 +21,16 @@
   cached block that follows different earlier blocks is not reused.  A
   prompt whose every block is cached still computes its last token (its
   logits are needed), in a block of its own.
+* Preemption by swapping ("03 -- ...", section "Preemption & eviction";
+  "Inside vLLM ...", section "Preemption Mechanics: Swapping vs.
+  Recomputation"): the swap-out and swap-in copies a step reports, applied to
+  the simulated pool and a simulated swap space, keep every token readable
+  through the tables, and a request swapped back in resumes where it
+  stopped; a small walkthrough pins the exact copies.
 Planted mistakes (budget not reduced by decode rows, a hit on a partial
 block, a wrong slot offset, a key without its parent, a hit on the block
-holding the last token) fail.
+holding the last token, swap-in pairs reversed, swap-outs not reported, a
+swapped-in request recomputed) fail.
 """
 import json
 import os
@@ -50,14 +57,27 @@ def _sample(req_id, pos):
     return (req_id * 7919 + pos * 104729 + 13) % 32000
 
 
-def run(s, steps, pool=None, B=None, check=True):
+def apply_swaps(batch, pool, host, B):
+    """The copies a step asks for, in the stated order: swap-outs (device
+    block -> host block), then swap-ins (host block -> device block)."""
+    for b, h in batch.swap_out:
+        for o in range(B):
+            host[(h, o)] = pool.get(b * B + o)
+    for h, b in batch.swap_in:
+        for o in range(B):
+            pool[b * B + o] = host.get((h, o))
+
+
+def run(s, steps, pool=None, B=None, check=True, host=None):
     """Drive ``steps`` steps; with ``pool`` (dict slot -> the tokens its K/V
     was computed from), write through the slots and check reads through
-    tables."""
+    tables; ``host`` is the swap space's content."""
     out = []
     for _ in range(steps):
         batch = s.step()
         out.append(batch)
+        if pool is not None and host is not None:
+            apply_swaps(batch, pool, host, B)
         by_id = {r.req_id: r for r in s.running}
         for e in batch.entries:
             r = by_id[e.req_id]
@@ -146,14 +166,17 @@ def block_prompt(rng, vocab_blocks, B):
     return prompt + [rng.randrange(50) for _ in range(rng.randrange(0, B + 1))]
 
 
-def _fuzz(seed, steps=60, num_blocks=48, max_new=10, block_vocab=False):
+def _fuzz(seed, steps=60, num_blocks=48, max_new=10, block_vocab=False, host_blocks=0):
     rng = random.Random(seed)
     B = 4
     s = sch.Scheduler(num_blocks=num_blocks, block_size=B, token_budget=24, chunk_tokens=8,
-                      free_order=rng.sample(range(num_blocks), num_blocks))
+                      free_order=rng.sample(range(num_blocks), num_blocks),
+                      num_host_blocks=host_blocks)
     prefixes = [[rng.randrange(50) for _ in range(rng.randrange(1, 14))] for _ in range(3)]
     vocab_blocks = [[rng.randrange(50) for _ in range(B)] for _ in range(3)]
-    pool = {}
+    pool, host = {}, {}
+    s.swap_ins = s.swap_outs = 0
+    at_swap_out = {}   # request -> tokens computed when it was swapped out
     nid = 0
     for _ in range(steps):
         for _ in range(rng.randrange(0, 3)):
@@ -164,8 +187,15 @@ def _fuzz(seed, steps=60, num_blocks=48, max_new=10, block_vocab=False):
                 prompt = pre + [rng.randrange(50) for _ in range(rng.randrange(1, 12))]
             s.add_request(nid, prompt, max_new_tokens=rng.randrange(1, max_new))
             nid += 1
-        batch = run(s, 1, pool, B)[0]
+        batch = run(s, 1, pool, B, host=host)[0]
         s.preemptions = getattr(s, "preemptions", 0) + len(batch.preempted)
+        s.swap_outs += len(batch.swapped_out)
+        s.swap_ins += len(batch.swap_in) > 0
+        for r in s.swapped:
+            at_swap_out.setdefault(r.req_id, r.num_computed)
+        for e in batch.entries:      # a swapped-in request resumes, not recomputes
+            if e.req_id in at_swap_out and e.req_id not in [r.req_id for r in s.swapped]:
+                assert e.seq_len - e.q_len == at_swap_out.pop(e.req_id), e.req_id
         n_dec = sum(1 for e in batch.entries if e.q_len == 1)
         assert sum(e.q_len for e in batch.entries if e.q_len > 1) <= max(0, 24 - n_dec) + 0
     return s
@@ -240,6 +270,37 @@ def check_full_prompt(a, b_entry, b, B=4):
 def test_fully_cached_prompt_computes_its_last_token():
     s = sch.Scheduler(num_blocks=32, block_size=4, token_budget=64, chunk_tokens=64)
     check_full_prompt(*full_prompt_case(s))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_swapping_restores_every_token(seed):
+    """Memory pressure with a swap space: preempted requests are swapped out
+    and back, every token still reads back through the tables after the
+    copies the steps asked for, and resumed requests are not recomputed."""
+    s = _fuzz(seed, steps=80, num_blocks=14, max_new=40, host_blocks=24)
+    assert s.swap_outs > 0 and s.swap_ins > 0
+
+
+def test_swap_walkthrough():
+    """Four device blocks of 4 tokens, a swap space of 2: B is swapped out
+    when A takes the last block, and swapped back into fresh blocks once A
+    has finished; B resumes at token 5 (the exact copies follow from the FIFO
+    free lists)."""
+    s = sch.Scheduler(num_blocks=4, block_size=4, token_budget=64, chunk_tokens=64,
+                      num_host_blocks=2)
+    s.add_request(0, list(range(1, 9)), max_new_tokens=3)    # A: 8 tokens, blocks 0, 1
+    s.add_request(1, [11, 12, 13, 14], max_new_tokens=8)     # B: 4 tokens, block 2
+    pool, host = {}, {}
+    batches = run(s, 5, pool, 4, host=host)
+    b1, b2, b3, b4, b5 = batches
+    assert [e.table for e in b1.entries] == [[0, 1], [2]]
+    assert b2.preempted == [1] and b2.swapped_out == [1] and b2.swap_out == [(2, 0)]
+    assert [e.table for e in b2.entries] == [[0, 1, 3]]
+    assert not b3.swap_in and not b4.swap_in          # A still holds three blocks
+    assert b5.swap_in == [(0, 2)]
+    (e,) = b5.entries
+    assert (e.req_id, e.q_len, e.seq_len, e.table) == (1, 1, 5, [2, 0])
+    assert e.slots == [0]
 
 
 def test_fuzz_under_memory_pressure_preempts_and_recovers():
@@ -324,6 +385,37 @@ def _all_pins():
         _fuzz(seed, block_vocab=True)
     test_prefix_key_names_the_whole_prefix()
     test_fully_cached_prompt_computes_its_last_token()
+
+
+def _swap_in_reversed(self, req, swap_in):
+    n = len(swap_in)
+    _orig_swap_in(self, req, swap_in)
+    swap_in[n:] = [(b, h) for h, b in swap_in[n:]]
+
+
+def _swap_out_not_reported(self, req, swap_out):
+    out = _orig_preempt(self, req, [])
+    return out
+
+
+def _swapped_request_recomputed(self, req, swap_in):
+    _orig_swap_in(self, req, swap_in)
+    req.num_computed = 0
+
+
+_orig_swap_in = sch.Scheduler._swap_in
+_orig_preempt = sch.Scheduler._preempt
+
+
+@pytest.mark.parametrize("name,bad", [("_swap_in", _swap_in_reversed),
+                                      ("_preempt", _swap_out_not_reported),
+                                      ("_swap_in", _swapped_request_recomputed)])
+def test_planted_swap_mistake_fails(monkeypatch, name, bad):
+    monkeypatch.setattr(sch.Scheduler, name, bad)
+    with pytest.raises((AssertionError, KeyError, IndexError, StopIteration)):
+        test_swap_walkthrough()
+        for seed in range(6):
+            _fuzz(seed, steps=80, num_blocks=14, max_new=40, host_blocks=24)
 
 
 @pytest.mark.parametrize("name,bad", [("step", _bad_budget), ("_lookup", _bad_lookup),

@@ -32,6 +32,9 @@ def _compare_step(ref, nat):
     for i, e in enumerate(b.entries):
         assert list(n["block_tables"][i, :len(e.table)]) == e.table
     assert list(n["preempted"]) == b.preempted
+    assert list(n["swapped_out"]) == b.swapped_out
+    assert [tuple(x) for x in n["swap_out"].tolist()] == [tuple(x) for x in b.swap_out]
+    assert [tuple(x) for x in n["swap_in"].tolist()] == [tuple(x) for x in b.swap_in]
     sampled = {e.req_id: _sample(e.req_id, e.seq_len) for e in b.entries}
     ref.update(b, sampled)
     nat.update(sampled)
@@ -41,9 +44,10 @@ def _compare_step(ref, nat):
     return b
 
 
-def _pair(num_blocks, B, budget, chunk, free_order=None):
-    return (sch.Scheduler(num_blocks, B, budget, chunk, free_order),
-            binding.BatchBuilder(num_blocks, B, budget, chunk, free_order))
+def _pair(num_blocks, B, budget, chunk, free_order=None, host_blocks=0):
+    return (sch.Scheduler(num_blocks, B, budget, chunk, free_order, num_host_blocks=host_blocks),
+            binding.BatchBuilder(num_blocks, B, budget, chunk, free_order,
+                                 num_host_blocks=host_blocks))
 
 
 def test_chunk_formula_example_native():
@@ -157,6 +161,41 @@ def test_repeated_block_streams_match(seed, num_blocks):
         _compare_step(ref, nat)
 
 
+def test_swap_walkthrough_native():
+    ref, nat = _pair(4, 4, 64, 64, host_blocks=2)
+    for s in (ref, nat):
+        s.add_request(0, list(range(1, 9)), 3)
+        s.add_request(1, [11, 12, 13, 14], 8)
+    swaps = []
+    for _ in range(8):
+        b = _compare_step(ref, nat)
+        swaps.append((b.swap_out, b.swap_in))
+    assert swaps[1] == ([(2, 0)], []) and swaps[4] == ([], [(0, 2)])
+
+
+@pytest.mark.parametrize("seed,num_blocks,host_blocks", [(s, 14, 24) for s in range(4)] +
+                         [(s, 10, 6) for s in range(2)] + [(s, 20, 64) for s in range(2)])
+def test_random_streams_with_swapping_match(seed, num_blocks, host_blocks):
+    """Memory pressure with a swap space (large enough, or too small for some
+    requests so that recomputation stays the fallback)."""
+    rng = random.Random(300 + seed)
+    B = 4
+    order = rng.sample(range(num_blocks), num_blocks)
+    ref, nat = _pair(num_blocks, B, 24, 8, order, host_blocks)
+    prefixes = [[rng.randrange(50) for _ in range(rng.randrange(1, 14))] for _ in range(3)]
+    nid = swaps = 0
+    for _ in range(80):
+        for _ in range(rng.randrange(0, 3)):
+            pre = rng.choice(prefixes) if rng.random() < 0.6 else []
+            prompt = pre + [rng.randrange(50) for _ in range(rng.randrange(1, 12))]
+            mn = rng.randrange(1, 40)
+            ref.add_request(nid, prompt, mn)
+            nat.add_request(nid, prompt, mn)
+            nid += 1
+        swaps += len(_compare_step(ref, nat).swapped_out)
+    assert swaps > 0
+
+
 def test_native_argument_errors():
     lib = binding.lib()
     assert not lib.pa_sched_create(0, 16, 64, 64, None)
@@ -175,3 +214,8 @@ def test_native_argument_errors():
     assert e.value.status == -6
     b.update({1: 9})
     assert list(out["seq_lens"]) == [2]
+    assert lib.pa_sched_enable_swap(b._h, 4) == -6        # requests already queued
+    fresh = binding.BatchBuilder(8, 4, 16, 16)
+    assert lib.pa_sched_enable_swap(fresh._h, -1) == -2
+    assert lib.pa_sched_enable_swap(fresh._h, 4) == 0
+    assert lib.pa_sched_enable_swap(fresh._h, 4) == -6    # once
