@@ -2293,57 +2293,78 @@ __global__ __launch_bounds__(256) void stage_offsets_kernel(AttnArgs a, int32_t*
   }
 }
 
-// Workgroup (j, s): logical block j of sequence s (a multi-token sequence)
-// into staging block off[s] + j, K and V of every KV head, and the staging
-// table entry.  Table entries past the sequence's blocks repeat its last
-// staging block; a staging block past the pool's capacity is not written
-// and the entry is clamped to the pool (out-of-contract capacities give
-// wrong results, never an access outside the pools).
-template <int D>
+// Workgroup b: staging block b, i.e. logical block j = b - off[s] of the
+// multi-token sequence s with off[s] <= b < off[s + 1] (found by bisection;
+// workgroups past off[S] or past the pool's capacity exit): K and V of every
+// KV head widened to bf16 with their scales, and the staging table entry of
+// (s, j).  The workgroup of a sequence's last block also fills its table
+// entries past its blocks with that block.  Each thread issues all of its
+// loads before it converts any.
+template <int D, int NKV>
 __global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_t* __restrict__ off,
                                                         int64_t cap, uint16_t* __restrict__ sk,
                                                         uint16_t* __restrict__ sv,
                                                         int32_t* __restrict__ stab) {
-  const int j = blockIdx.x;
-  const int s = blockIdx.y;
-  int r0, qn;
-  seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
-  if (qn <= 1) return;
-  const int nblk = table_blocks(a.seq_lens[s], a.log2_block, a.max_blocks);
-  const int64_t base = off[s];
-  if (threadIdx.x == 0) {
-    const int64_t e = min(base + min(j, max(nblk - 1, 0)), max(cap - 1, (int64_t)0));
-    stab[(int64_t)s * a.max_blocks + j] = (int32_t)e;
+  const int64_t bidx = blockIdx.x;
+  const int S = a.num_seqs;
+  if (bidx >= off[S] || bidx >= cap) return;
+  int lo = 0, hi = S - 1;  // the last sequence s with off[s] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= bidx) lo = mid;
+    else hi = mid - 1;
   }
-  if (j >= nblk || base + j >= cap) return;
-  const int64_t dst = base + j;
+  const int s = lo;
+  const int j = (int)(bidx - off[s]);
+  const int nblk = off[s + 1] - off[s];   // > j: sequence s owns staging block b
+  int32_t* trow = stab + (int64_t)s * a.max_blocks;
+  if (threadIdx.x == 0) trow[j] = (int32_t)bidx;
+  if (j == nblk - 1)
+    for (int x = nblk + threadIdx.x; x < a.max_blocks; x += 256) trow[x] = (int32_t)bidx;
   const int phys = clampi(a.block_tables[(int64_t)s * a.max_blocks + j], 0, a.num_blocks - 1);
   const int Hkv = a.num_kv_heads;
   const int64_t tile = (int64_t)D << a.log2_block;  // elements of one (block, KV head) tile
   const int64_t n = Hkv * tile;
   const uint8_t* k8 = static_cast<const uint8_t*>(a.k_cache) + phys * n;
   const uint8_t* v8 = static_cast<const uint8_t*>(a.v_cache) + phys * n;
-  uint16_t* k16 = sk + dst * n;
-  uint16_t* v16 = sv + dst * n;
-  for (int64_t e = (int64_t)threadIdx.x * 16; e < n; e += 256 * 16) {
-    const int h = (int)(e / tile);  // 16 elements never straddle a tile (tile % 16 == 0)
-    const float ks = a.k_scales[(int64_t)phys * Hkv + h];
-    const float vs = a.v_scales[(int64_t)phys * Hkv + h];
+  uint16_t* k16 = sk + bidx * n;
+  uint16_t* v16 = sv + bidx * n;
+  // NKV 16-byte pieces per thread and pool cover the block when n == NKV * 256 * 16
+  // (8 KV heads of D x B bytes, B * D = 2048); other sizes loop.
+  for (int64_t e0 = (int64_t)threadIdx.x * 16; e0 < n; e0 += (int64_t)NKV * 256 * 16) {
+    u32x4 ck[NKV], cv[NKV];
 #pragma unroll
-    for (int pool = 0; pool < 2; ++pool) {
-      const u32x4 c = *reinterpret_cast<const u32x4*>((pool ? v8 : k8) + e);
-      const float sc = pool ? vs : ks;
-      uint32_t w[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], false);
-        const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], true);
-        w[2 * q] = f32_to_bf16_bits(lo2[0] * sc) | ((uint32_t)f32_to_bf16_bits(lo2[1] * sc) << 16);
-        w[2 * q + 1] = f32_to_bf16_bits(hi2[0] * sc) | ((uint32_t)f32_to_bf16_bits(hi2[1] * sc) << 16);
+    for (int u = 0; u < NKV; ++u) {
+      const int64_t e = e0 + (int64_t)u * 256 * 16;
+      if (e < n) {
+        ck[u] = *reinterpret_cast<const u32x4*>(k8 + e);
+        cv[u] = *reinterpret_cast<const u32x4*>(v8 + e);
       }
-      u32x4* d = reinterpret_cast<u32x4*>((pool ? v16 : k16) + e);
-      d[0] = u32x4{w[0], w[1], w[2], w[3]};
-      d[1] = u32x4{w[4], w[5], w[6], w[7]};
+    }
+#pragma unroll
+    for (int u = 0; u < NKV; ++u) {
+      const int64_t e = e0 + (int64_t)u * 256 * 16;
+      if (e >= n) continue;
+      const int h = (int)(e / tile);  // 16 elements never straddle a tile (tile % 16 == 0)
+      const float ks = a.k_scales[(int64_t)phys * Hkv + h];
+      const float vs = a.v_scales[(int64_t)phys * Hkv + h];
+#pragma unroll
+      for (int pool = 0; pool < 2; ++pool) {
+        const u32x4 c = pool ? cv[u] : ck[u];
+        const float sc = pool ? vs : ks;
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], false);
+          const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], true);
+          w[2 * q] = f32_to_bf16_bits(lo2[0] * sc) | ((uint32_t)f32_to_bf16_bits(lo2[1] * sc) << 16);
+          w[2 * q + 1] =
+              f32_to_bf16_bits(hi2[0] * sc) | ((uint32_t)f32_to_bf16_bits(hi2[1] * sc) << 16);
+        }
+        u32x4* d = reinterpret_cast<u32x4*>((pool ? v16 : k16) + e);
+        d[0] = u32x4{w[0], w[1], w[2], w[3]};
+        d[1] = u32x4{w[4], w[5], w[6], w[7]};
+      }
     }
   }
 }
@@ -2354,8 +2375,8 @@ hipError_t launch_chunked_fp8_d(const AttnArgs& dec, const AttnArgs& chunk, void
   stage_offsets_kernel<<<1, 256, 0, st>>>(dec, off);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (dec.max_query_len > 1) {
-    stage_fp8_kernel<D><<<dim3(dec.max_blocks, dec.num_seqs), 256, 0, st>>>(
+  if (dec.max_query_len > 1 && cap > 0) {
+    stage_fp8_kernel<D, 4><<<(unsigned)cap, 256, 0, st>>>(
         dec, off, cap, static_cast<uint16_t*>(const_cast<void*>(chunk.k_cache)),
         static_cast<uint16_t*>(const_cast<void*>(chunk.v_cache)),
         const_cast<int32_t*>(chunk.block_tables));
