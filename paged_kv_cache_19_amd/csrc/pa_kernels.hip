@@ -1095,14 +1095,13 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
   int* P = smem;           // [S + 1] steps before entry s (per KV head)
   int* Ls = smem + S + 1;  // [S]     sequence lengths
   const int lane = threadIdx.x;
-  const int w = blockIdx.x;
   decode_prefix_fill<FP8>(a, P, Ls, lane, 64);
   __syncthreads();
   decode_prefix_scan(P, S, lane);
   __syncthreads();
   const int64_t N = (int64_t)a.num_kv_heads * P[S];
   const int64_t weff = N == 0 ? 0 : min((int64_t)waves, max((int64_t)1, N / kMinStepsPerWave));
-  if (w == 0) {
+  if (blockIdx.x == 0) {
     if (lane == 0) {
       hdr->total_steps = N;
       hdr->waves = weff;
@@ -1110,7 +1109,13 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
     int* hp = reinterpret_cast<int*>(hdr + 1);
     for (int s = lane; s <= S; s += 64) hp[s] = P[s];
   }
-  if (w >= weff) return;
+  if ((int64_t)blockIdx.x >= weff) return;
+  // Workgroups are dealt to the 8 XCDs round-robin; each XCD takes a
+  // contiguous run of the weff shares, so the KV heads of one sequence
+  // (neighbours in the work list) run under one L2 and share its lines of
+  // the block table and of the fp8 scales.  A bijection of [0, weff).
+  const int nb = (int)weff, xq = nb >> 3, xr = nb & 7, xk = blockIdx.x & 7;
+  const int w = xk * xq + min(xk, xr) + (blockIdx.x >> 3);
   decode_share<D, FP8, kDecodeSets, PREFIX>(a, P, Ls, N, weff, w);
 }
 
