@@ -27,6 +27,10 @@
 //   chunk_mix_kernel<D>          the query chunks and the single-token rows
 //                                of one call in one persistent launch, the
 //                                CUs split between the two kinds of work
+//   chunk_mix_fp8_kernel<D>      the same over an e4m3 cache (chunk units on
+//                                bf16-staged blocks)
+//   stage_offsets_kernel, stage_fp8_kernel<D>
+//                                the staging of those blocks
 //   attn_mfma_kernel<D>          fixed-split bf16 decode
 //   attn_valu_kernel<ES, D>      fp32 (and small-block bf16) split-K attention
 //                                on the vector ALUs
@@ -625,7 +629,7 @@ __device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p) {
 constexpr int kDecodeSets = 3;
 constexpr int kFp8Sets = 3;
 
-template <int D, bool STREAM, int R = 1>
+template <int D, bool STREAM, int R = 1, int NSETS = kFp8Sets>
 __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, int kv_wave,
                                            int kv_min, int k_begin, int k_end,
                                            RowState<D, R>& st) {
@@ -766,21 +770,21 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
   };
 
   // Steps below k_safe need no mask; at most one step (the last) does.
-  // A ring of kFp8Sets fragment sets: the loads of step i + kFp8Sets - 1 are
-  // issued before step i is computed, so kFp8Sets - 1 steps are in flight
+  // A ring of NSETS fragment sets: the loads of step i + NSETS - 1 are
+  // issued before step i is computed, so NSETS - 1 steps are in flight
   // while the wave computes; steps past the end are not loaded.
   const int k_safe = max(k_begin, min(k_end, (min(kv_min, kv_wave) - k_begin) / 64 * 64 + k_begin));
   const int n = (k_end - k_begin + 63) >> 6;
-  KVFrag8<D> f[kFp8Sets];
+  KVFrag8<D> f[NSETS];
 #pragma unroll
-  for (int p = 0; p < kFp8Sets - 1; ++p)
+  for (int p = 0; p < NSETS - 1; ++p)
     if (p < n) load(f[p], k_begin + 64 * p);
-  for (int i0 = 0; i0 < n; i0 += kFp8Sets) {
+  for (int i0 = 0; i0 < n; i0 += NSETS) {
 #pragma unroll
-    for (int j = 0; j < kFp8Sets; ++j) {
+    for (int j = 0; j < NSETS; ++j) {
       const int i = i0 + j;
       if (i >= n) break;
-      if (i + kFp8Sets - 1 < n) load(f[(j + kFp8Sets - 1) % kFp8Sets], k_begin + 64 * (i + kFp8Sets - 1));
+      if (i + NSETS - 1 < n) load(f[(j + NSETS - 1) % NSETS], k_begin + 64 * (i + NSETS - 1));
       const int c = k_begin + 64 * i;
       compute(f[j], c, c + 64 > k_safe);
     }
@@ -1063,9 +1067,9 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
                      : k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) & ~(STEP - 1)
                                                       : 0;
     if constexpr (FP8) {
-      if (k_sh > k_begin) attend_fp8<D, false>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+      if (k_sh > k_begin) attend_fp8<D, false, 1, NSETS>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
       if (k_end > max(k_begin, k_sh))
-        attend_fp8<D, true>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+        attend_fp8<D, true, 1, NSETS>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
     } else {
       if (k_sh > k_begin)
         attend<D, 1, false, NSETS>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
@@ -1116,7 +1120,7 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
   // the block table and of the fp8 scales.  A bijection of [0, weff).
   const int nb = (int)weff, xq = nb >> 3, xr = nb & 7, xk = blockIdx.x & 7;
   const int w = xk * xq + min(xk, xr) + (blockIdx.x >> 3);
-  decode_share<D, FP8, kDecodeSets, PREFIX>(a, P, Ls, N, weff, w);
+  decode_share<D, FP8, FP8 ? kFp8Sets : kDecodeSets, PREFIX>(a, P, Ls, N, weff, w);
 }
 
 // Up to kMergeBatch pieces of one row held in registers, so that all of
@@ -1865,32 +1869,39 @@ void prefill_kernel(AttnArgs a, int num_wgs) {
 // is within 1.5-3% of the best split found by sweeping it.
 constexpr int64_t kChunkStepNs = 1650;
 constexpr int64_t kDecodeStepNs = 770;
+// An e4m3 decode step (64 keys, the same 16 KiB) in the fused launch runs
+// with two fragment sets in a 256-register budget: on workload 5 over e4m3
+// pools, 1,000 ns gave the fastest call of 600-1,700 ns, with the Infinity
+// Cache flushed between calls and without.
+constexpr int64_t kDecodeStepNsFp8 = 1000;
 
-template <int D>
-__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
-    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
-void chunk_mix_kernel(AttnArgs a, int num_wgs, StreamKHeader* hdr) {
+// dec holds the single-token rows' view (the e4m3 pools when FP8), chunk the
+// chunk units' view (the same arguments for a bf16 cache; for e4m3 the
+// staged bf16 pools and their table).
+template <int D, bool FP8>
+__device__ __forceinline__ void chunk_mix_body(const AttnArgs& dec, const AttnArgs& chunk,
+                                               int num_wgs, StreamKHeader* hdr) {
   constexpr int NW = PrefillShape<D>::kWaves;
   static_assert(PrefillShape<D>::kHalves == 1, "decode waves need the two-wave register budget");
   extern __shared__ int lds_i[];
-  const int S = a.num_seqs;
+  const int S = dec.num_seqs;
   int* seq_prefix = lds_i;        // [S + 1] chunk steps before sequence s
   int* P = lds_i + S + 1;         // [S + 1] decode steps before sequence s (per KV head)
   int* Ls = P + S + 1;            // [S]     sequence lengths
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  decode_prefix_fill<false>(a, P, Ls, tid, 64 * NW);
-  prefill_prefix<D>(a, seq_prefix);  // synchronises: P and Ls are filled too
+  decode_prefix_fill<FP8>(dec, P, Ls, tid, 64 * NW);
+  prefill_prefix<D>(chunk, seq_prefix);  // synchronises: P and Ls are filled too
   if (w == 0) decode_prefix_scan(P, S, lane);
   __syncthreads();
   const int64_t n_pf = seq_prefix[S];
-  const int64_t n_dec = (int64_t)a.num_kv_heads * P[S];
+  const int64_t n_dec = (int64_t)dec.num_kv_heads * P[S];
   int w_dec = 0;
   if (n_dec > 0) {
     const int64_t pf = n_pf * (kChunkStepNs * D / 128);
-    const int64_t dec = n_dec * (kDecodeStepNs * D / 128);
-    w_dec = (int)(((int64_t)num_wgs * dec / (pf + dec) + 4) / 8 * 8);
+    const int64_t dc = n_dec * ((FP8 ? kDecodeStepNsFp8 : kDecodeStepNs) * D / 128);
+    w_dec = (int)(((int64_t)num_wgs * dc / (pf + dc) + 4) / 8 * 8);
     w_dec = max(w_dec, 8);
     if (n_pf > 0) w_dec = min(w_dec, num_wgs - 8);
   }
@@ -1900,7 +1911,7 @@ void chunk_mix_kernel(AttnArgs a, int num_wgs, StreamKHeader* hdr) {
       hdr->total_steps = 0;
       hdr->waves = 0;
     }
-    prefill_ranges_any<D>(a, seq_prefix, blockIdx.x, w_pf);
+    prefill_ranges_any<D>(chunk, seq_prefix, blockIdx.x, w_pf);
     return;
   }
   const int64_t waves = (int64_t)w_dec * NW;
@@ -1915,7 +1926,23 @@ void chunk_mix_kernel(AttnArgs a, int num_wgs, StreamKHeader* hdr) {
     for (int s = lane; s <= S; s += 64) hp[s] = P[s];
   }
   if (dw >= weff) return;
-  decode_share<D, false, 2>(a, P, Ls, n_dec, weff, dw);
+  decode_share<D, FP8, 2>(dec, P, Ls, n_dec, weff, dw);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
+    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
+void chunk_mix_kernel(AttnArgs a, int num_wgs, StreamKHeader* hdr) {
+  chunk_mix_body<D, false>(a, a, num_wgs, hdr);
+}
+
+// The same over an e4m3 cache: chunk units on the staged bf16 pools, the
+// single-token rows on the e4m3 pools (two fragment sets per decode wave).
+template <int D>
+__global__ __launch_bounds__(64 * PrefillShape<D>::kWaves) __attribute__((
+    amdgpu_waves_per_eu(PrefillShape<D>::kHalves == 1 ? 2 : 1, PrefillShape<D>::kHalves == 1 ? 2 : 1)))
+void chunk_mix_fp8_kernel(AttnArgs dec, AttnArgs chunk, int num_wgs, StreamKHeader* hdr) {
+  chunk_mix_body<D, true>(dec, chunk, num_wgs, hdr);
 }
 
 // ---------------------------------------------------------------------------
@@ -2210,6 +2237,25 @@ hipError_t launch_mix(const AttnArgs& a, void* header, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The e4m3 call's chunk units (staged pools) and decode rows in one launch.
+template <int D>
+hipError_t launch_mix_fp8(const AttnArgs& dec, const AttnArgs& chunk, void* header,
+                          hipStream_t st) {
+  static thread_local Residency cache;
+  const size_t lds = (size_t)(3 * dec.num_seqs + 2) * sizeof(int);
+  int n = 0;
+  hipError_t err = resident(cache, chunk_mix_fp8_kernel<D>, 64 * PrefillShape<D>::kWaves, lds,
+                            dec.num_seqs, n);
+  if (err != hipSuccess) return err;
+  n = n >= 16 ? n / 8 * 8 : 16;  // both kinds of work get whole multiples of 8
+  StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
+  chunk_mix_fp8_kernel<D><<<n, 64 * PrefillShape<D>::kWaves, lds, st>>>(dec, chunk, n, hdr);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  merge_streamk_kernel<2, D><<<dim3((dec.num_q_heads + 3) / 4, dec.num_seqs), 256, 0, st>>>(dec, hdr);
+  return hipGetLastError();
+}
+
 template <int ES, int D>
 hipError_t launch_merge(const AttnArgs& a, int skip_single, hipStream_t st) {
   merge_kernel<ES, D><<<dim3((a.num_q_heads + 3) / 4, a.num_tokens), 256, 0, st>>>(a, skip_single);
@@ -2260,7 +2306,8 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
 // every multi-token sequence are first staged as bf16 (value(code) * scale,
 // rounded to nearest even) into a staging pool, and the bf16 chunk kernel
 // runs on that pool.  Single-token rows read the e4m3 pools directly through
-// the e4m3 balanced decode.
+// the e4m3 balanced decode, in the same launch as the chunk units
+// (chunk_mix_fp8_kernel) up to kMaxMixSeqs sequences, else after them.
 // ---------------------------------------------------------------------------
 
 // Staged blocks of sequence s: nblk(s) = its table blocks when it has more
@@ -2299,12 +2346,14 @@ __global__ __launch_bounds__(256) void stage_offsets_kernel(AttnArgs a, int32_t*
 }
 
 // Workgroup b: staging block b, i.e. logical block j = b - off[s] of the
-// multi-token sequence s with off[s] <= b < off[s + 1] (found by bisection;
-// workgroups past off[S] or past the pool's capacity exit): K and V of every
-// KV head widened to bf16 with their scales, and the staging table entry of
-// (s, j).  The workgroup of a sequence's last block also fills its table
-// entries past its blocks with that block.  Each thread issues all of its
-// loads before it converts any.
+// multi-token sequence s with off[s] <= b < off[s + 1] (workgroups past
+// off[S] or past the pool's capacity exit): K and V of every KV head widened
+// to bf16 with their scales, and the staging table entry of (s, j).  The
+// workgroup of a sequence's last block also fills its table entries past its
+// blocks with that block.  The sequence is found by a 256-way search (every
+// thread probes one offset per level: one level up to 256 sequences, two up
+// to 65,536), and each thread issues its K, V and scale loads together
+// before it converts any.
 template <int D, int NKV>
 __global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_t* __restrict__ off,
                                                         int64_t cap, uint16_t* __restrict__ sk,
@@ -2313,11 +2362,16 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_
   const int64_t bidx = blockIdx.x;
   const int S = a.num_seqs;
   if (bidx >= off[S] || bidx >= cap) return;
-  int lo = 0, hi = S - 1;  // the last sequence s with off[s] <= b
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= bidx) lo = mid;
-    else hi = mid - 1;
+  // the last sequence s with off[s] <= b: off is non-decreasing, so the
+  // probes at or below b form a prefix; [lo, hi) always holds the answer
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 255) >> 8;
+    const int idx = lo + (int)threadIdx.x * step;
+    const int cnt = __syncthreads_count(idx < hi && off[idx] <= bidx);  // >= 1: off[lo] <= b
+    const int nlo = lo + (cnt - 1) * step;
+    hi = min(lo + cnt * step, hi);
+    lo = nlo;
   }
   const int s = lo;
   const int j = (int)(bidx - off[s]);
@@ -2332,31 +2386,34 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_
   const int64_t n = Hkv * tile;
   const uint8_t* k8 = static_cast<const uint8_t*>(a.k_cache) + phys * n;
   const uint8_t* v8 = static_cast<const uint8_t*>(a.v_cache) + phys * n;
+  const float* ksc = a.k_scales + (int64_t)phys * Hkv;
+  const float* vsc = a.v_scales + (int64_t)phys * Hkv;
   uint16_t* k16 = sk + bidx * n;
   uint16_t* v16 = sv + bidx * n;
   // NKV 16-byte pieces per thread and pool cover the block when n == NKV * 256 * 16
   // (8 KV heads of D x B bytes, B * D = 2048); other sizes loop.
   for (int64_t e0 = (int64_t)threadIdx.x * 16; e0 < n; e0 += (int64_t)NKV * 256 * 16) {
     u32x4 ck[NKV], cv[NKV];
+    float ks[NKV], vs[NKV];
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
       const int64_t e = e0 + (int64_t)u * 256 * 16;
       if (e < n) {
+        const int h = (int)(e / tile);  // 16 elements never straddle a tile (tile % 16 == 0)
         ck[u] = *reinterpret_cast<const u32x4*>(k8 + e);
         cv[u] = *reinterpret_cast<const u32x4*>(v8 + e);
+        ks[u] = ksc[h];
+        vs[u] = vsc[h];
       }
     }
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
       const int64_t e = e0 + (int64_t)u * 256 * 16;
       if (e >= n) continue;
-      const int h = (int)(e / tile);  // 16 elements never straddle a tile (tile % 16 == 0)
-      const float ks = a.k_scales[(int64_t)phys * Hkv + h];
-      const float vs = a.v_scales[(int64_t)phys * Hkv + h];
 #pragma unroll
       for (int pool = 0; pool < 2; ++pool) {
         const u32x4 c = pool ? cv[u] : ck[u];
-        const float sc = pool ? vs : ks;
+        const float sc = pool ? vs[u] : ks[u];
         uint32_t w[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -2387,10 +2444,15 @@ hipError_t launch_chunked_fp8_d(const AttnArgs& dec, const AttnArgs& chunk, void
         const_cast<int32_t*>(chunk.block_tables));
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = launch_prefill<D>(chunk, st);
+    // as for a bf16 cache: one launch for both kinds of rows when the
+    // prefix sums fit next to the LDS ring
+    err = dec.num_seqs <= kMaxMixSeqs ? launch_mix_fp8<D>(dec, chunk, header, st)
+                                      : launch_prefill<D>(chunk, st);
     if (err != hipSuccess) return err;
+    if (dec.num_seqs > kMaxMixSeqs) err = launch_streamk<D, true>(dec, header, st);
+  } else {
+    err = launch_streamk<D, true>(dec, header, st);
   }
-  err = launch_streamk<D, true>(dec, header, st);
   if (err != hipSuccess) return err;
   return chunk.max_splits > 1 ? launch_merge<2, D>(chunk, 1, st) : hipSuccess;
 }
