@@ -2390,42 +2390,42 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_
   const float* vsc = a.v_scales + (int64_t)phys * Hkv;
   uint16_t* k16 = sk + bidx * n;
   uint16_t* v16 = sv + bidx * n;
-  // NKV 16-byte pieces per thread and pool cover the block when n == NKV * 256 * 16
-  // (8 KV heads of D x B bytes, B * D = 2048); other sizes loop.
-  for (int64_t e0 = (int64_t)threadIdx.x * 16; e0 < n; e0 += (int64_t)NKV * 256 * 16) {
-    u32x4 ck[NKV], cv[NKV];
+  // NKV 8-byte pieces per thread and pool cover the block when n == NKV * 256 * 8
+  // (8 KV heads of D x B bytes, B * D = 2048); other sizes loop.  Each
+  // load and each 16-byte store instruction covers one contiguous run.
+  for (int64_t e0 = (int64_t)threadIdx.x * 8; e0 < n; e0 += (int64_t)NKV * 256 * 8) {
+    uint2 ck[NKV], cv[NKV];
     float ks[NKV], vs[NKV];
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
-      const int64_t e = e0 + (int64_t)u * 256 * 16;
+      const int64_t e = e0 + (int64_t)u * 256 * 8;
       if (e < n) {
-        const int h = (int)(e / tile);  // 16 elements never straddle a tile (tile % 16 == 0)
-        ck[u] = *reinterpret_cast<const u32x4*>(k8 + e);
-        cv[u] = *reinterpret_cast<const u32x4*>(v8 + e);
+        const int h = (int)(e / tile);  // 8 elements never straddle a tile (tile % 8 == 0)
+        ck[u] = *reinterpret_cast<const uint2*>(k8 + e);
+        cv[u] = *reinterpret_cast<const uint2*>(v8 + e);
         ks[u] = ksc[h];
         vs[u] = vsc[h];
       }
     }
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
-      const int64_t e = e0 + (int64_t)u * 256 * 16;
+      const int64_t e = e0 + (int64_t)u * 256 * 8;
       if (e >= n) continue;
 #pragma unroll
       for (int pool = 0; pool < 2; ++pool) {
-        const u32x4 c = pool ? cv[u] : ck[u];
+        const uint2 c = pool ? cv[u] : ck[u];
         const float sc = pool ? vs[u] : ks[u];
-        uint32_t w[8];
+        uint32_t w[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], false);
-          const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(c[q], true);
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t cq = q ? c.y : c.x;
+          const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(cq, false);
+          const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(cq, true);
           w[2 * q] = f32_to_bf16_bits(lo2[0] * sc) | ((uint32_t)f32_to_bf16_bits(lo2[1] * sc) << 16);
           w[2 * q + 1] =
               f32_to_bf16_bits(hi2[0] * sc) | ((uint32_t)f32_to_bf16_bits(hi2[1] * sc) << 16);
         }
-        u32x4* d = reinterpret_cast<u32x4*>((pool ? v16 : k16) + e);
-        d[0] = u32x4{w[0], w[1], w[2], w[3]};
-        d[1] = u32x4{w[4], w[5], w[6], w[7]};
+        *reinterpret_cast<u32x4*>((pool ? v16 : k16) + e) = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
   }
@@ -2438,7 +2438,7 @@ hipError_t launch_chunked_fp8_d(const AttnArgs& dec, const AttnArgs& chunk, void
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (dec.max_query_len > 1 && cap > 0) {
-    stage_fp8_kernel<D, 4><<<(unsigned)cap, 256, 0, st>>>(
+    stage_fp8_kernel<D, 8><<<(unsigned)cap, 256, 0, st>>>(
         dec, off, cap, static_cast<uint16_t*>(const_cast<void*>(chunk.k_cache)),
         static_cast<uint16_t*>(const_cast<void*>(chunk.v_cache)),
         const_cast<int32_t*>(chunk.block_tables));
