@@ -278,6 +278,25 @@ def test_fp8_chunked_prefill_edge_cases(case):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("n_dec", [1012, 1088], ids=["fused-at-1024-seqs", "two-launches-1100-seqs"])
+def test_fp8_chunked_prefill_around_the_fused_launch_limit(n_dec):
+    """12 chunk sequences plus single-token rows: 1,024 sequences in all is
+    the most the fused chunk + e4m3 decode launch takes, 1,100 run the chunk
+    units and the e4m3 decode as two launches; every row either way."""
+    shape = workloads.Shape("fp8-many", workloads.BF16, 32, 8, 128, 16)
+    n_chunk = 12
+    lens = [300 + 25 * i for i in range(n_chunk)] + [20 + (7 * i) % 100 for i in range(n_dec)]
+    qls = [40 + 5 * i for i in range(n_chunk)] + [1] * n_dec
+    log(f"[fp8 chunked many] {len(lens)} sequences, {n_chunk} chunks")
+    wl = workloads.make_workload(2, seed=94, device="cuda", seq_lens=lens, q_lens=qls,
+                                 shape=shape, kv_fp8=True)
+    _, err = _run_fp8_chunked(wl)
+    log(f"[fp8 chunked many] max abs err {err:.3e}")
+    assert err <= TOL
+    del wl
+    torch.cuda.empty_cache()
+
+
 def test_fp8_chunked_prefill_checks_its_staging_room(monkeypatch):
     shape = workloads.Shape("fp8-chunk-room", workloads.BF16, 8, 2, 128, 16)
     wl = workloads.make_workload(2, seed=79, device="cuda", seq_lens=[300, 40], q_lens=[64, 1],
