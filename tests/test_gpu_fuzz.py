@@ -1,0 +1,93 @@
+"""Seeded random shapes through every attention entry point.
+
+Each case draws the KV head count, the group size G (odd ones included),
+head_dim, the block size, the batch size and every sequence's length and
+query length (decode rows, or a mix with query chunks), then runs the
+slot mapping, the cache write and the attention on the GPU and compares
+every row with the oracle, at the same bar as the fixed cases: 2e-2
+max-abs for a bf16 or e4m3 cache, 1e-4 for fp32.  The oracle's cost is
+capped per case so that the file runs in about a minute."""
+import random
+
+import pytest
+
+from paged_kv_cache_19_amd import workloads
+from tests.gpu_common import TOL, log, run_and_compare
+from tests.test_gpu_fp8 import TOL as TOL8
+from tests.test_gpu_fp8 import _run_fp8, _run_fp8_chunked
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 12
+MAX_ORACLE_MACS = 1.5e9   # sum over query rows and heads of seq_len * head_dim
+
+
+def draw(kind: str, i: int):
+    """(Hq, Hkv, D, B, seq_lens, q_lens) of case i of one kind."""
+    rng = random.Random({"bf16": 1000, "f32": 2000, "fp8": 3000, "fp8chunk": 4000}[kind] + i)
+    while True:
+        Hkv = rng.choice([1, 2, 4, 8])
+        G = rng.choice([g for g in (1, 2, 3, 4, 5, 8, 16) if Hkv * g <= 32])
+        D = rng.choice([64, 128])
+        if kind == "f32":
+            B = rng.choice([1, 2, 4, 8, 16])
+        elif kind == "bf16":
+            B = rng.choice([8, 16, 32, 64])
+        else:
+            B = rng.choice([16, 32, 64])
+        S = rng.randint(1, 24)
+        lens = [rng.choice([rng.randint(1, 64), rng.randint(1, 700), rng.randint(1, 4000)])
+                for _ in range(S)]
+        if kind in ("f32", "bf16") and rng.random() < 0.5 or kind == "fp8chunk":
+            qls = [rng.choice([1, 1, rng.randint(1, min(L, 128))]) for L in lens]
+            if kind == "fp8chunk" and max(qls) == 1:
+                qls[0] = min(lens[0], 2) if lens[0] >= 2 else 1
+                if max(qls) == 1:
+                    continue
+        else:
+            qls = [1] * S
+        cost = sum(q * L for q, L in zip(qls, lens)) * G * Hkv * D
+        if cost <= MAX_ORACLE_MACS:
+            return Hkv * G, Hkv, D, B, lens, qls
+
+
+def _workload(kind, i, fp8=False):
+    Hq, Hkv, D, B, lens, qls = draw(kind, i)
+    dtype = workloads.F32 if kind == "f32" else workloads.BF16
+    log(f"[fuzz {kind} {i}] Hq={Hq} Hkv={Hkv} D={D} B={B} S={len(lens)} "
+        f"rows={sum(qls)} max_len={max(lens)} max_q={max(qls)}")
+    shape = workloads.Shape(f"fuzz-{kind}", dtype, Hq, Hkv, D, B)
+    return workloads.make_workload(2, seed=500 + i, device="cuda", seq_lens=lens, q_lens=qls,
+                                   shape=shape, kv_fp8=fp8)
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"bf16-{i}" for i in range(N_CASES)])
+def test_fuzz_bf16(i):
+    wl = _workload("bf16", i)
+    _, err = run_and_compare(wl)
+    log(f"[fuzz bf16 {i}] max abs err {err:.3e}")
+    assert err <= TOL[workloads.BF16]
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"f32-{i}" for i in range(N_CASES)])
+def test_fuzz_f32(i):
+    wl = _workload("f32", i)
+    _, err = run_and_compare(wl)
+    log(f"[fuzz f32 {i}] max abs err {err:.3e}")
+    assert err <= TOL[workloads.F32]
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"fp8-{i}" for i in range(N_CASES)])
+def test_fuzz_fp8_decode(i):
+    wl = _workload("fp8", i, fp8=True)
+    _, err = _run_fp8(wl)
+    log(f"[fuzz fp8 {i}] max abs err {err:.3e}")
+    assert err <= TOL8
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"fp8chunk-{i}" for i in range(N_CASES)])
+def test_fuzz_fp8_chunked(i):
+    wl = _workload("fp8chunk", i, fp8=True)
+    _, err = _run_fp8_chunked(wl)
+    log(f"[fuzz fp8 chunked {i}] max abs err {err:.3e}")
+    assert err <= TOL8
