@@ -1,7 +1,7 @@
 """The random shapes of the GPU fuzz cases (tests/test_gpu_fuzz.py) reach
 what they are meant to: both head_dims on every path, both kinds of batch,
 odd group sizes, and an oracle cost within the cap.  CPU only."""
-from tests.test_gpu_fuzz import MAX_ORACLE_MACS, N_CASES, draw
+from tests.test_gpu_fuzz import MAX_ORACLE_MACS, N_CASES, draw, draw_shared
 
 KINDS = ("bf16", "f32", "fp8", "fp8chunk")
 
@@ -36,3 +36,21 @@ def test_fuzz_draws_cover_the_shapes():
         assert ("bf16", "B", B) in seen, B
     for B in (1, 4):
         assert ("f32", "B", B) in seen, B
+
+
+def test_shared_prefix_draws():
+    seen = set()
+    for fp8 in (False, True):
+        for i in range(N_CASES):
+            Hq, Hkv, D, B, prefix, lens = draw_shared(fp8, i)
+            assert draw_shared(fp8, i) == (Hq, Hkv, D, B, prefix, lens)
+            assert prefix % B == 0 and prefix >= B and min(lens) > prefix
+            assert sum(lens) * Hq * D <= MAX_ORACLE_MACS
+            step = 64 if fp8 else 32
+            seen.add((fp8, "D", D))
+            seen.add((fp8, "prefix under a step", prefix < step))
+            seen.add((fp8, "one sequence", len(lens) == 1))
+            seen.add((fp8, "many", len(lens) >= 16))
+    for fp8 in (False, True):
+        assert (fp8, "D", 64) in seen and (fp8, "D", 128) in seen
+        assert (fp8, "many", True) in seen

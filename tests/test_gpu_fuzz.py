@@ -15,6 +15,8 @@ from paged_kv_cache_19_amd import workloads
 from tests.gpu_common import TOL, log, run_and_compare
 from tests.test_gpu_fp8 import TOL as TOL8
 from tests.test_gpu_fp8 import _run_fp8, _run_fp8_chunked
+from tests.test_gpu_shared_prefix import TOL as TOL_SP
+from tests.test_gpu_shared_prefix import _run as _run_shared
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +51,24 @@ def draw(kind: str, i: int):
         cost = sum(q * L for q, L in zip(qls, lens)) * G * Hkv * D
         if cost <= MAX_ORACLE_MACS:
             return Hkv * G, Hkv, D, B, lens, qls
+
+
+def draw_shared(fp8: bool, i: int):
+    """(Hq, Hkv, D, B, prefix tokens, seq_lens) of shared-prefix case i: every
+    table starts with the same prefix blocks, and every sequence has at least
+    one position past them (the slot of this step's token)."""
+    rng = random.Random((6000 if fp8 else 5000) + i)
+    while True:
+        Hkv = rng.choice([1, 2, 4, 8])
+        G = rng.choice([g for g in (1, 2, 3, 4, 5, 8, 16) if Hkv * g <= 32])
+        D = rng.choice([64, 128])
+        B = rng.choice([16, 32, 64] if fp8 else [8, 16, 32, 64])
+        prefix = B * rng.randint(1, max(1, 2500 // B))
+        S = rng.randint(1, 40)
+        lens = [prefix + rng.choice([1, rng.randint(1, 64), rng.randint(1, 1500)])
+                for _ in range(S)]
+        if sum(lens) * G * Hkv * D <= MAX_ORACLE_MACS:
+            return Hkv * G, Hkv, D, B, prefix, lens
 
 
 def _workload(kind, i, fp8=False):
@@ -91,3 +111,17 @@ def test_fuzz_fp8_chunked(i):
     _, err = _run_fp8_chunked(wl)
     log(f"[fuzz fp8 chunked {i}] max abs err {err:.3e}")
     assert err <= TOL8
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"shared-{i}" for i in range(N_CASES)])
+def test_fuzz_shared_prefix(i, fp8):
+    Hq, Hkv, D, B, prefix, lens = draw_shared(fp8, i)
+    log(f"[fuzz shared {'fp8' if fp8 else 'bf16'} {i}] Hq={Hq} Hkv={Hkv} D={D} B={B} "
+        f"prefix={prefix} S={len(lens)} max_len={max(lens)}")
+    shape = workloads.Shape("fuzz-shared", workloads.BF16, Hq, Hkv, D, B)
+    wl = workloads.make_workload(2, seed=600 + i, device="cuda", seq_lens=lens, shape=shape,
+                                 shared_prefix_tokens=prefix, kv_fp8=fp8)
+    _, err, diff = _run_shared(wl, prefix // B, fp8=fp8)
+    log(f"[fuzz shared {i}] max abs err {err:.3e}, vs plain decode {diff:.3e}")
+    assert err <= TOL_SP and diff <= TOL_SP
