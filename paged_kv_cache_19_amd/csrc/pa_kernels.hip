@@ -2401,8 +2401,12 @@ __global__ __launch_bounds__(256) void stage_fp8_kernel(AttnArgs a, const int32_
       const int64_t e = e0 + (int64_t)u * 256 * 8;
       if (e < n) {
         const int h = (int)(e / tile);  // 8 elements never straddle a tile (tile % 8 == 0)
-        ck[u] = *reinterpret_cast<const uint2*>(k8 + e);
-        cv[u] = *reinterpret_cast<const uint2*>(v8 + e);
+        // the codes are read once: streamed past the caches (the staged
+        // copies are written through them, for the chunk kernel to re-read)
+        const uint64_t k64 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(k8 + e));
+        const uint64_t v64 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(v8 + e));
+        ck[u] = make_uint2((uint32_t)k64, (uint32_t)(k64 >> 32));
+        cv[u] = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
         ks[u] = ksc[h];
         vs[u] = vsc[h];
       }
