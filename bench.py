@@ -446,8 +446,9 @@ def main():
         achieved = (f_chunk + f_single) / (attn_avg * 1e-3) / 1e12
         roofline = {
             "kernel": ("pa_chunked_prefill_fp8: the query-chunk sequences' blocks staged as "
-                       "bf16, the chunk kernel (MFMA) on them, the e4m3 balanced decode of the "
-                       "single-token rows, then the merges") if fp8 else
+                       "bf16, then one persistent launch splitting the CUs between the "
+                       "query-chunk units (MFMA, on the staged blocks) and the e4m3 balanced "
+                       "decode of the single-token rows, then the merges") if fp8 else
                       ("pa_chunked_prefill: one persistent launch splitting the CUs between "
                        "the query-chunk units (MFMA) and the balanced decode of the "
                        "single-token rows, then the merges"),
@@ -458,7 +459,7 @@ def main():
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "flops_per_launch": f_chunk + f_single,
             "avg_launch_ms": round(attn_avg, 5),
-            "traffic": None,
+            "traffic": measured_traffic(workload_name, call),
         }
     else:
         achieved = call_bytes / (attn_avg * 1e-3) / 1e9
