@@ -24,6 +24,10 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns once it is enqueued, so
  *    stream order gives slot mapping -> cache write -> attention.
+ *  - No entry point synchronises the stream, allocates device memory or
+ *    memsets on its own (PA_CHECK=1 below aside), so a step -- cache write
+ *    and attention, with output and workspace allocated beforehand -- can
+ *    be captured in a HIP graph and replayed.
  *  - The return value is a pa_status, known synchronously.  Argument
  *    checks (null pointers, sizes, head counts, dtype, workspace size) are
  *    made before anything is enqueued.  A failed launch returns PA_ERR_HIP.
