@@ -20,9 +20,13 @@ Prints ONE JSON line.  ``value`` is the step's KV-read throughput in GB/s
 HBM peak ride along.  ``roofline`` covers the attention call (the dominant
 one), timed with HIP events on the stream its kernels run on: HBM-bound for
 decode, MFMA-bound (bf16 dense peak) for the chunked-prefill mix.
-``roofline.ceiling`` is the second denominator: the read rate of a probe
-that gathers random 4 KiB tiles (one K or V tile of a block and KV head)
-from a 4 GiB pool with the decode's loads, measured in the same run.
+``roofline.ceiling`` is the second denominator, measured in the same run:
+for decode the read rate of a probe that gathers random 4 KiB tiles (one K
+or V tile of a block and KV head) from a 4 GiB pool with the decode's loads;
+for the chunked-prefill mix the rate of back-to-back
+v_mfma_f32_32x32x16_bf16, the chunk kernel's instruction.  ``--tp N`` runs
+one tensor-parallel rank's share of a workload: the same sequences with
+H_q / N query and H_kv / N KV heads.
 ``cache_write`` times pa_reshape_and_cache (and the slot mapping) on their
 own.  By default the 256 MB Infinity Cache is flushed before every step,
 outside the timed events, so no step reads what the step before left there
@@ -147,6 +151,44 @@ def read_ceiling(dev, reps=5):
                                    f"non-temporal 16-byte loads; median of {reps} reads")
 
 
+def mfma_ceiling(dev, reps=5):
+    """TFLOP/s of back-to-back v_mfma_f32_32x32x16_bf16 (libpa_probe.so):
+    two workgroups of four waves per CU, four independent accumulators per
+    wave.  Returns (median TFLOP/s, description) or (None, reason)."""
+    import ctypes
+
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        return None, "libpa_probe.so not built"
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.pa_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 8192
+    flops = wgs * 4 * iters * 4 * 2 * 32 * 32 * 16
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    warm = 20  # about 20 ms of matrix work first: the clock ramps up under it
+    rates = []
+    for k in range(warm + reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = fn(sink.data_ptr(), wgs, iters, ctypes.c_void_p(stream.cuda_stream))
+        b.record(stream)
+        if rc != 0:
+            return None, f"probe returned {rc}"
+        if k >= warm:
+            torch.cuda.synchronize()
+            rates.append(flops / (a.elapsed_time(b) * 1e-3) / 1e12)
+    torch.cuda.synchronize()
+    del sink
+    return percentile(rates, 50), (f"back-to-back v_mfma_f32_32x32x16_bf16, {wgs} workgroups "
+                                   f"of 4 waves, 4 accumulators per wave, after {warm} untimed "
+                                   f"runs; median of {reps} runs")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -179,7 +221,10 @@ def parse():
                         "by the step before; ms_per_step is then the mean of per-step events "
                         "(default on; --no-flush times back-to-back steps)")
     p.add_argument("--no-ceiling", action="store_true",
-                   help="skip the random-tile read probe (the roofline's second denominator)")
+                   help="skip the ceiling probe (the roofline's second denominator)")
+    p.add_argument("--tp", type=int, default=1,
+                   help="one tensor-parallel rank's share: H_q / tp query and H_kv / tp KV "
+                        "heads of the workload (tp divides H_kv)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="also run one plain device copy of BYTES bytes (a reference for "
                         "hardware byte counters)")
@@ -305,7 +350,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()  # raises if libpa.so is missing
     dev = "cuda"
-    wl = workloads.make_workload(args.workload, device=dev, kv_fp8=fp8)
+    shape = None
+    if args.tp != 1:
+        base = workloads.SHAPES[args.workload]
+        if args.tp < 1 or base.num_kv_heads % args.tp:
+            print(f"--tp must divide the workload's {base.num_kv_heads} KV heads", file=sys.stderr)
+            sys.exit(2)
+        shape = workloads.Shape(base.name.replace("-bf16", f"-tp{args.tp}-rank-bf16"),
+                                base.dtype, base.num_q_heads // args.tp,
+                                base.num_kv_heads // args.tp, base.head_dim, base.block_size)
+    wl = workloads.make_workload(args.workload, device=dev, kv_fp8=fp8, shape=shape)
     shp = wl.shape
     t = wl.tensors
     bt = wl.block_tables_tensor(dev)
@@ -434,10 +488,18 @@ def main():
     e_in = 2 if shp.dtype == "bf16" else 4
     e_out = 1 if fp8 else e_in
     write_bytes = 2 * T * shp.num_kv_heads * shp.head_dim * (e_in + e_out) + 8 * T
-    ceiling, ceiling_how = (None, "skipped") if args.no_ceiling else read_ceiling(dev)
-    if ceiling is not None:
-        print(f"[bench] read ceiling {ceiling:.1f} GB/s ({ceiling_how})", file=sys.stderr,
-              flush=True)
+    if args.no_ceiling:
+        ceiling, ceiling_how = None, "skipped"
+    elif chunked:
+        ceiling, ceiling_how = mfma_ceiling(dev)
+        if ceiling is not None:
+            print(f"[bench] MFMA ceiling {ceiling:.1f} TFLOP/s ({ceiling_how})", file=sys.stderr,
+                  flush=True)
+    else:
+        ceiling, ceiling_how = read_ceiling(dev)
+        if ceiling is not None:
+            print(f"[bench] read ceiling {ceiling:.1f} GB/s ({ceiling_how})", file=sys.stderr,
+                  flush=True)
     kv_bytes, call_bytes = algorithmic_bytes(wl, args.kv_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     workload_name = shp.name if not fp8 else shp.name.replace("-bf16", "-fp8kv")
@@ -460,6 +522,11 @@ def main():
             "flops_per_launch": f_chunk + f_single,
             "avg_launch_ms": round(attn_avg, 5),
             "traffic": measured_traffic(workload_name, call),
+            "ceiling": None if ceiling is None else {
+                "what": ceiling_how,
+                "achieved_over_ceiling": round(achieved / ceiling, 4),
+                "tflops": round(ceiling, 1),
+            },
         }
     else:
         achieved = call_bytes / (attn_avg * 1e-3) / 1e9
@@ -505,6 +572,7 @@ def main():
             "block_size": shp.block_size,
             "kv_cache": args.kv_dtype,
             "seq_lens": SEQ_LENS[args.workload],
+            "tensor_parallel_rank_of": args.tp,
             "seed": wl.seed,
             "total_tokens": sum(wl.seq_lens),
             "kv_bytes": kv_bytes,

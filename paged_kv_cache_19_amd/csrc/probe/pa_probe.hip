@@ -1,4 +1,4 @@
-// libpa_probe: a measurement probe for bench.py, not part of libpa's ABI.
+// libpa_probe: measurement probes for bench.py, not part of libpa's ABI.
 //
 // pa_probe_read_tiles reads whole tiles of a device pool in a random order
 // (the tile ids are a permutation the caller draws) with the same access
@@ -8,6 +8,12 @@
 // reach on the device -- the second denominator bench.py reports beside the
 // nominal HBM peak.  Every load stays inside the pool: tile ids are taken
 // modulo the number of tiles, and each lane reads offsets below tile_bytes.
+//
+// pa_probe_mfma issues v_mfma_f32_32x32x16_bf16 back to back (four
+// independent accumulators per wave, two waves per SIMD), the instruction
+// the chunked-prefill kernel runs on.  Its flops / time is the matrix-core
+// rate the device sustains, the second denominator beside the 2.5 PFLOP/s
+// dense bf16 peak.  It touches no memory but one sink word per thread.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,6 +54,34 @@ __global__ __launch_bounds__(256) void read_tiles_kernel(const u32x4* __restrict
   sink[wave * kWaveLanes + lane] = acc;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kMfmaChains = 4;
+
+__global__ __launch_bounds__(256) void mfma_kernel(int32_t iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & (kWaveLanes - 1);
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(0.001f * (float)(lane + e));
+    b[e] = static_cast<__bf16>(0.002f * (float)(lane - e));
+  }
+  f32x16 acc[kMfmaChains];
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k) acc[k] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < kMfmaChains; ++k)
+      acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t += acc[k][r];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = t;
+}
+
 template <int TILE_BYTES>
 hipError_t launch(const void* pool, const int32_t* ids, int32_t num_ids, int32_t num_tiles,
                   uint32_t* sink, int32_t num_waves, hipStream_t st) {
@@ -81,4 +115,15 @@ extern "C" int pa_probe_read_tiles(const void* pool, int64_t pool_bytes, const i
     default: return -2;
   }
   return e == hipSuccess ? 0 : -7;
+}
+
+// Runs num_wgs workgroups of 256 threads, each wave issuing iters x 4
+// v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 multiply-adds each); `sink`
+// receives one float per thread (float [num_wgs * 256]).  Returns 0, -2 for
+// bad sizes, -7 when the launch fails.
+extern "C" int pa_probe_mfma(float* sink, int32_t num_wgs, int32_t iters, void* stream) {
+  if (!sink || num_wgs <= 0 || iters <= 0) return -2;
+  hipLaunchKernelGGL(mfma_kernel, dim3(num_wgs), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }

@@ -28,6 +28,23 @@ def test_workload_parity(cfg):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cfg,tp", [(3, 8), (5, 8), (2, 2)], ids=["70b-tp8", "mix-tp8", "8b-tp2"])
+def test_tensor_parallel_rank_shape(cfg, tp):
+    """One tensor-parallel rank's share of a workload (bench.py --tp): the
+    same sequences with H_q / tp query and H_kv / tp KV heads (at tp = 8 a
+    single KV head); every row."""
+    base = workloads.SHAPES[cfg]
+    shape = workloads.Shape(base.name + f"-tp{tp}", base.dtype, base.num_q_heads // tp,
+                            base.num_kv_heads // tp, base.head_dim, base.block_size)
+    log(f"[tp rank] workload {cfg} at tp={tp}: H_q={shape.num_q_heads} H_kv={shape.num_kv_heads}")
+    wl = workloads.make_workload(cfg, device="cuda", shape=shape)
+    out, err = run_and_compare(wl)
+    log(f"[tp rank] max abs err {err:.3e}")
+    assert err <= TOL[wl.shape.dtype]
+    del wl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("split", [64, 128, 512, 1024])
 def test_split_counts_agree(split):
     wl = workloads.make_workload(2, device="cuda", seq_lens=[1, 63, 64, 65, 700, 2048, 4000, 4096],
