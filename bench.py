@@ -17,8 +17,10 @@ entry points).
 
 Prints ONE JSON line.  ``value`` is the step's KV-read throughput in GB/s
 (algorithmic KV bytes / step time); tokens/s and the fraction of the 8 TB/s
-HBM peak ride along.  ``roofline`` covers the attention call (the dominant
-one), timed with HIP events on the stream its kernels run on: HBM-bound for
+HBM peak ride along.  The K timed steps carry no event between their
+kernels; a second pass of K steps under the same conditions times the
+parts.  ``roofline`` covers the attention call (the dominant one), timed
+there with HIP events on the stream its kernels run on: HBM-bound for
 decode, MFMA-bound (bf16 dense peak) for the chunked-prefill mix.
 ``roofline.ceiling`` is the second denominator, measured in the same run:
 for decode the read rate of a probe that gathers random 4 KiB tiles (one K
@@ -453,23 +455,34 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    def pairs():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    # The timed region: exactly K steps, each bracketed by its own two events
+    # (so that the flushes between steps can be left out) and nothing inside
+    # it, so that no event record sits between the step's kernels.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)]
-    wevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    sevs = pairs()
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        step(evs[k], sevs[k], wevs[k])
+        step(sev=sevs[k])
     stop.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
     if args.flush:  # the flushes are not part of the step
         ms_step = sum(a.elapsed_time(b) for a, b in sevs) / args.steps
+    # The parts of the step: K more steps under the same conditions, with
+    # events around the attention call, the cache write and the slot mapping.
+    evs, sevs2 = pairs(), pairs()
+    wevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(evs[k], sevs2[k], wevs[k])
+    torch.cuda.synchronize()
+    sevs = sevs2
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg = sum(attn_ms) / len(attn_ms)
     slot_ms = [a[0].elapsed_time(w) for a, w in zip(sevs, wevs)]
