@@ -219,7 +219,8 @@ size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
  * q_len == 1 are decode rows and may be mixed in freely.
  * max_query_len must be >= every q_len and num_tokens == qsl[num_seqs].
  * block_refcounts and scale: as for pa_decode.  On the bf16 path at most
- * 2048 sequences per call (PA_ERR_UNSUPPORTED above that).
+ * 2048 sequences per call, and K / V pools under 2^40 bytes each
+ * (PA_ERR_UNSUPPORTED otherwise).
  */
 int pa_chunked_prefill(void* out, const void* query, const void* k_cache,
                        const void* v_cache, const int32_t* block_tables,
@@ -358,7 +359,9 @@ size_t pa_chunked_prefill_fp8_workspace_bytes(int32_t num_seqs, int32_t num_toke
  * knows it); >= 1 when max_query_len > 1, else PA_ERR_SHAPE.  A batch that
  * needs more is PA_ERR_INDEX under PA_CHECK=1; without it, the blocks past
  * the room are not staged and those rows are undefined (every access stays
- * inside the pools).  block_size 16, 32 or 64; at most 2048 sequences.
+ * inside the pools).  block_size 16, 32 or 64; at most 2048 sequences;
+ * each bf16 staging pool (chunk_context_blocks blocks) under 2^40 bytes
+ * (PA_ERR_UNSUPPORTED otherwise).
  * Other arguments, errors and the workspace ownership as for
  * pa_chunked_prefill and pa_decode_fp8.
  */

@@ -23,6 +23,9 @@ constexpr int kMinChunkSteps = 16;
 constexpr int kChunkPieces = 4;
 // The balanced decode keeps every sequence's step prefix sum in LDS.
 constexpr int kMaxBalancedSeqs = 4096;
+// Largest K or V pool the chunk kernel takes (block offsets in 256-byte
+// units in one dword).
+constexpr int64_t kMaxChunkPoolBytes = (int64_t)1 << 40;
 constexpr size_t kAlign = 256;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -278,6 +281,11 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   const bool mfma = pa::mfma_path(a);
   const int G = num_q_heads / num_kv_heads;
   if (mfma && chunk_entry && num_seqs > pa::kMaxChunkSeqs) return PA_ERR_UNSUPPORTED;
+  // The chunk kernel holds a block's offset in the pool as one dword of
+  // 256-byte units.
+  if (mfma && chunk_entry &&
+      (int64_t)num_blocks * num_kv_heads * block_size * head_dim * 2 >= kMaxChunkPoolBytes)
+    return PA_ERR_UNSUPPORTED;
   const int64_t tiles_y = mfma ? ((int64_t)G + 15) / 16 : max_query_len;
   if (tiles_y > 65535 || (int64_t)num_tokens > 65535 * 64) return PA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -753,6 +761,10 @@ int pa_chunked_prefill_fp8(void* out, const void* query, const void* k_cache,
   if ((int64_t)num_seqs * num_kv_heads > 65535 || (int64_t)num_tokens > 65535 * 64)
     return PA_ERR_UNSUPPORTED;
   if (chunk_context_blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  // the chunk kernel reads the bf16 staging pools (one dword of 256-byte
+  // units per block offset)
+  if (chunk_context_blocks * num_kv_heads * block_size * head_dim * 2 >= kMaxChunkPoolBytes)
+    return PA_ERR_UNSUPPORTED;
   // query chunks need a staging pool of at least one block (every staging
   // table entry is clamped into it)
   if (max_query_len > 1 && chunk_context_blocks < 1) return PA_ERR_SHAPE;

@@ -1384,7 +1384,7 @@ __device__ __forceinline__ void prefill_prefix(const AttnArgs& a, int* seq_prefi
 // CPB is the number of 8-key chunks one block holds inside a 32-key step
 // (min(B, 32) / 8): fixed at compile time, so the V^T tile's head_dim tiles
 // sit at constant offsets from a lane's read address.
-template <int D, int CPB>
+template <int D, int LGB>
 __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq_prefix, int wg,
                                                int num_wgs, uint16_t (*smem)[2][32 * D]) {
   constexpr int H = PrefillShape<D>::kHalves;    // 32-row halves per wave
@@ -1408,10 +1408,10 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
   const int S = a.num_seqs;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int Hkv = a.num_kv_heads;
-  const int lg = a.log2_block;
-  const int B = 1 << lg;
-  constexpr int Bs = 8 * CPB;    // keys of one block inside a step
-  constexpr int cpb = CPB;       // 8-key chunks of one block inside a step (1, 2, 4)
+  constexpr int lg = LGB;        // block size B = 2^LGB, 8 to 64 on this path
+  constexpr int B = 1 << lg;
+  constexpr int cpb = (B < 32 ? B : 32) / 8;  // 8-key chunks of one block inside a step (1, 2, 4)
+  constexpr int Bs = 8 * cpb;    // keys of one block inside a step
   constexpr int lcpb = cpb == 4 ? 2 : cpb - 1;
 
   const int N = seq_prefix[S];
@@ -1428,7 +1428,7 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
     const int chunk16 = (lane % CPR) ^ ksw<D>(t);
     k_voff[x2] = ((lane / CPR) * D + chunk16 * 8) * 2;
     const int p = 64 * x + lane;              // 16-byte position in the V^T tile
-    v_bi[x2] = p / (D * cpb);                 // block of the step
+    v_bi[x2] = __builtin_amdgcn_readfirstlane(p / (D * cpb));  // block of the step (wave-uniform)
     const int d = (p % (D * cpb)) >> lcpb;    // head_dim row
     const int vs = (d >> (4 - lcpb)) & (cpb - 1);
     const int u = (p & (cpb - 1)) ^ vs;       // 8-key chunk inside the block
@@ -1540,19 +1540,16 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
       // Block ids: a window of 64 logical blocks, one per lane, read with
       // readlane.  Ids are clamped when a window becomes current, not when it
       // is loaded: the prefetched next window is not waited for early.  The
-      // current window is kept as each block's byte offset in the pool (two
-      // dwords per lane), so a load's block base is two readlanes and an add.
+      // current window is kept as each block's offset in the pool in 256-byte
+      // units (a block is a multiple of 256 bytes, and the host keeps the
+      // pool under 2^40 bytes), so a load's block base is one readlane, a
+      // shift and an add.
       auto window = [&](int b0) { return a.block_tables[trow + min(b0 + lane, a.max_blocks - 1)]; };
-      const uint64_t blk_bytes = (uint64_t)blk_stride * 2;
-      uint32_t woff_lo, woff_hi;
-      auto set_window = [&](int id) {
-        const uint64_t off = (uint64_t)(uint32_t)clampi(id, 0, a.num_blocks - 1) * blk_bytes;
-        woff_lo = (uint32_t)off;
-        woff_hi = (uint32_t)(off >> 32);
-      };
+      const uint32_t blk_units = (uint32_t)(blk_stride * 2 / 256);
+      uint32_t woff;
+      auto set_window = [&](int id) { woff = (uint32_t)clampi(id, 0, a.num_blocks - 1) * blk_units; };
       auto block_off = [&](int idx) {
-        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(woff_hi, idx) << 32) |
-               (uint64_t)(uint32_t)__builtin_amdgcn_readlane(woff_lo, idx);
+        return (uint64_t)(uint32_t)__builtin_amdgcn_readlane(woff, idx) << 8;
       };
       int blk0 = k_begin >> lg;
       set_window(window(blk0));
@@ -1579,9 +1576,8 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
                                  kbase + (cin + ((x * RPI) & (Bs - 1))) * D) +
                              block_off(min(cb + kb, cmax));
           load_to_lds(ksrc + k_voff[x2], &smem[st][0][x * 512]);
-          const int vb = __builtin_amdgcn_readfirstlane(v_bi[x2]);
           const char* vsrc =
-              reinterpret_cast<const char*>(vbase + cin) + block_off(min(cb + vb, cmax));
+              reinterpret_cast<const char*>(vbase + cin) + block_off(min(cb + v_bi[x2], cmax));
           load_to_lds(vsrc + v_voff[x2], &smem[st][1][x * 512]);
         }
       };
@@ -1832,10 +1828,12 @@ __device__ __forceinline__ void prefill_ranges_any(const AttnArgs& a, const int*
                                                    int wg, int num_wgs) {
   // The ring of K / V^T stages (one per workgroup, whatever the block size).
   __shared__ __attribute__((aligned(16))) uint16_t smem[kPrefillStages][2][32 * D];
-  const int cpb = min(1 << a.log2_block, 32) >> 3;
-  if (cpb == 1) prefill_ranges<D, 1>(a, seq_prefix, wg, num_wgs, smem);
-  else if (cpb == 2) prefill_ranges<D, 2>(a, seq_prefix, wg, num_wgs, smem);
-  else prefill_ranges<D, 4>(a, seq_prefix, wg, num_wgs, smem);
+  switch (a.log2_block) {
+    case 3: prefill_ranges<D, 3>(a, seq_prefix, wg, num_wgs, smem); break;
+    case 4: prefill_ranges<D, 4>(a, seq_prefix, wg, num_wgs, smem); break;
+    case 5: prefill_ranges<D, 5>(a, seq_prefix, wg, num_wgs, smem); break;
+    default: prefill_ranges<D, 6>(a, seq_prefix, wg, num_wgs, smem); break;
+  }
 }
 
 template <int D>

@@ -136,6 +136,19 @@ def test_other_entry_points_reject_bad_arguments(lib):
     args[8] = FAKE
     args[21] = None
     assert cp(*args) == -5
+    # the chunk kernel takes K / V pools under 2^40 bytes: 2^27 blocks of
+    # 2 x 16 x 128 bf16 make 2^40 bytes (refused before any device access)
+    args[21] = FAKE
+    args[17] = 1 << 27
+    assert cp(*args) == -4
+    # pa_chunked_prefill_fp8: the same limit on each bf16 staging pool
+    f8 = lib.pa_chunked_prefill_fp8
+    f8args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, 2, 10, 64, 8, 8, 2,
+              128, 16, 8, 1 << 27, 0.1, FAKE, 1 << 30, None]
+    assert f8(*f8args) == -4
+    f8args[20] = (1 << 27) - 1
+    f8args[23] = 16
+    assert f8(*f8args) == -5
 
 
 def _shared(lib, **kw):
