@@ -122,6 +122,7 @@ EDGE = [
     ("bf16", 32, 8, 64, 32, [4000, 70, 2500], None),             # head_dim 64, B = 32
     ("bf16", 8, 2, 128, 8, [300, 90], [150, 2]),                 # chunks, B = 8
     ("bf16", 8, 2, 128, 64, [700, 130], [300, 64]),              # chunks, B = 64
+    ("bf16", 8, 2, 128, 32, [700, 130, 9], [300, 32, 1]),        # chunks, B = 32
     ("bf16", 8, 2, 64, 16, [500, 33], [257, 33]),                # chunks, head_dim 64, B = 16
     ("bf16", 32, 8, 128, 16, [3000, 2500, 7], [1000, 700, 1]),   # long chunks, many row tiles
     ("bf16", 8, 2, 64, 8, [300, 90], [150, 2]),                  # chunks, head_dim 64, B = 8
