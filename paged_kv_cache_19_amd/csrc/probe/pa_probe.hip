@@ -9,6 +9,10 @@
 // nominal HBM peak.  Every load stays inside the pool: tile ids are taken
 // modulo the number of tiles, and each lane reads offsets below tile_bytes.
 //
+// pa_probe_read_rows reads the same kind of tiles (4 KiB) in the layout of an
+// MFMA A operand, 64 bytes of each of 16 rows per load, as the decode reads
+// K: the L1 then sends 64-byte requests instead of whole 128-byte lines.
+//
 // pa_probe_mfma issues v_mfma_f32_32x32x16_bf16 back to back (four
 // independent accumulators per wave, two waves per SIMD), the instruction
 // the chunked-prefill kernel runs on.  Its flops / time is the matrix-core
@@ -58,6 +62,39 @@ __global__ __launch_bounds__(256) void read_tiles_kernel(const u32x4* __restrict
     for (int u = 0; u < kTilesInFlight; ++u)
 #pragma unroll
       for (int k = 0; k < kPerLane; ++k) acc ^= v[u][k].x ^ v[u][k].y ^ v[u][k].z ^ v[u][k].w;
+  }
+  sink[wave * kWaveLanes + lane] = acc;
+}
+
+// The same random 4 KiB tiles (16 rows of 256 bytes, a bf16 K tile of one
+// block and KV head) read in the layout of an MFMA A operand: load k gives
+// lane (i, j) = (l % 16, l / 16) bytes 64k + 16j .. +15 of row i, so every
+// load reads 64 bytes of each of 16 rows (the decode's K loads).
+__global__ __launch_bounds__(256) void read_rows_kernel(const char* __restrict__ pool,
+                                                        const int32_t* __restrict__ tile_ids,
+                                                        int32_t num_ids, int32_t num_tiles,
+                                                        uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & (kWaveLanes - 1);
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWaveLanes;
+  const int num_waves = gridDim.x * blockDim.x / kWaveLanes;
+  const int off = (lane & 15) * 256 + (lane >> 4) * 16;
+  uint32_t acc = 0;
+  for (int t0 = wave * kTilesInFlight; t0 < num_ids; t0 += num_waves * kTilesInFlight) {
+    u32x4 v[kTilesInFlight][4];
+#pragma unroll
+    for (int u = 0; u < kTilesInFlight; ++u) {
+      const int t = t0 + u;
+      const int id = t < num_ids ? (int)((uint32_t)tile_ids[t] % (uint32_t)num_tiles) : -1;
+      const char* base = pool + (int64_t)(id < 0 ? 0 : id) * 4096 + off;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[u][k] = id >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 64 * k))
+                          : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kTilesInFlight; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc ^= v[u][k].x ^ v[u][k].y ^ v[u][k].z ^ v[u][k].w;
   }
   sink[wave * kWaveLanes + lane] = acc;
 }
@@ -229,6 +266,21 @@ extern "C" int pa_probe_read_tiles(const void* pool, int64_t pool_bytes, const i
     default: return -2;
   }
   return e == hipSuccess ? 0 : -7;
+}
+
+// pa_probe_read_tiles with 4 KiB tiles, read in the MFMA A-operand layout
+// (read_rows_kernel: 64 bytes of each of 16 rows per load instead of 1 KiB
+// contiguous).  Same arguments and returns, without tile_bytes.
+extern "C" int pa_probe_read_rows(const void* pool, int64_t pool_bytes, const int32_t* tile_ids,
+                                  int32_t num_ids, uint32_t* sink, int32_t num_waves,
+                                  void* stream) {
+  if (!pool || !tile_ids || !sink || num_ids <= 0 || num_waves <= 0 || num_waves % 4 != 0)
+    return -2;
+  if (pool_bytes < 4096 || pool_bytes / 4096 > INT32_MAX) return -2;
+  hipLaunchKernelGGL(read_rows_kernel, dim3(num_waves / 4), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const char*>(pool), tile_ids,
+                     num_ids, (int32_t)(pool_bytes / 4096), sink);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 // Runs num_wgs workgroups of 256 threads, each wave issuing iters x 4

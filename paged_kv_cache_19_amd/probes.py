@@ -8,6 +8,8 @@ builder-written kernels of ``libpa_probe.so`` (``csrc/probe/pa_probe.hip``):
 - the read rate of random tiles from a 4 GiB pool, over tile sizes and wave
   counts (four tiles in flight per wave): how the rate depends on the bytes in
   flight across the chip;
+- the same for 4 KiB tiles read in two load layouts, 1 KiB contiguous per
+  load and 64 bytes of each of 16 rows per load (an MFMA A operand);
 - the rate of back-to-back ``v_mfma_f32_32x32x16_bf16``;
 - how matrix and vector work overlap on a SIMD: bursts of 8 MFMAs and of a
   softmax-like vector mix, alone, one after the other in each wave,
@@ -35,6 +37,10 @@ def _lib():
     lib.pa_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_void_p]
+    lib.pa_probe_read_rows.restype = ctypes.c_int
+    lib.pa_probe_read_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p]
     lib.pa_probe_mfma.restype = ctypes.c_int
     lib.pa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p]
@@ -85,6 +91,31 @@ def read_rates(lib, pool_bytes: int = 4 << 30):
     return rows
 
 
+def read_layouts(lib, pool_bytes: int = 4 << 30):
+    """GB/s of random 4 KiB tiles read 1 KiB contiguous per load, and read
+    64 bytes of each of 16 rows per load (the MFMA A-operand layout)."""
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096 * 64, dtype=torch.int32, device="cuda")
+    n = pool_bytes // 4096
+    ids = torch.randperm(n, dtype=torch.int32, device="cuda",
+                         generator=torch.Generator(device="cuda").manual_seed(7))
+    rows = []
+    for name, call in (("1 KiB contiguous per load", lambda w, s: lib.pa_probe_read_tiles(
+                            pool.data_ptr(), pool_bytes, ids.data_ptr(), n, 4096, sink.data_ptr(),
+                            w, s)),
+                       ("64 B of each of 16 rows per load", lambda w, s: lib.pa_probe_read_rows(
+                            pool.data_ptr(), pool_bytes, ids.data_ptr(), n, sink.data_ptr(), w,
+                            s))):
+        row = [name]
+        for waves in (1024, 2048, 4096):
+            ms = _time_ms(lambda s: call(waves, s), 4, 1)
+            row.append(pool_bytes / (ms * 1e-3) / 1e9)
+        rows.append(row)
+    del pool, sink, ids
+    torch.cuda.empty_cache()
+    return rows
+
+
 def mfma_rate(lib, iters: int = 8192):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs = 2 * cus
@@ -117,6 +148,12 @@ def main() -> None:
     print("|---|---|---|---|")
     for tile, *r in read_rates(lib):
         print(f"| {tile // 1024} KiB | " + " | ".join(f"{x:.0f}" for x in r) + " |")
+    print("\n## Random 4 KiB tiles (16 rows of 256 B) by load layout (GB/s; four tiles in flight "
+          "per wave)\n")
+    print("| layout | 1,024 waves | 2,048 waves | 4,096 waves |")
+    print("|---|---|---|---|")
+    for name, *r in read_layouts(lib):
+        print(f"| {name} | " + " | ".join(f"{x:.0f}" for x in r) + " |")
     cold, warm = mfma_rate(lib)
     print("\n## Back-to-back v_mfma_f32_32x32x16_bf16 (two workgroups of four waves per CU, "
           "four accumulators per wave)\n")
