@@ -664,6 +664,12 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
       wid = wid_next;
       wid_next = window(blk0 + 64);
     }
+    // The scales go out first: loads complete in issue order, so the
+    // step's scores wait for its K loads only, not for its V loads too.
+    const int pv = c + 16 * j4;
+    const int bv = block_id(pv);
+    f.ks = a.k_scales[(int64_t)bv * Hkv + v.kvh];
+    f.vs = a.v_scales[(int64_t)bv * Hkv + v.kvh];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int pos = c + tok_k + 4 * x;
@@ -671,13 +677,9 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
 #pragma unroll
       for (int p = 0; p < KP; ++p) f.k[x][p] = load_u32x4<STREAM>(kp + 16 * p);
     }
-    const int pv = c + 16 * j4;
-    const int bv = block_id(pv);
     const uint8_t* vp = vbase + bv * blk_stride + (pv & (B - 1));
 #pragma unroll
     for (int n = 0; n < NT; ++n) f.v[n] = load_u32x4<STREAM>(vp + (int64_t)16 * n * B);
-    f.ks = a.k_scales[(int64_t)bv * Hkv + v.kvh];
-    f.vs = a.v_scales[(int64_t)bv * Hkv + v.kvh];
   };
 
   // mask: the step holds keys at or past kv_min (scores masked to -inf)
