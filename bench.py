@@ -3,8 +3,14 @@
 
 One step = the whole hot path over one synthetic batch, through the C ABI:
 slot mapping for the new tokens, the cache write of their K/V, and paged
-attention (pa_decode, or pa_chunked_prefill for the prefill + decode mix).
-Inputs are resident in HBM before the timed region.
+attention.  For the decode workloads that is one pa_decode_append call
+(pa_decode_fp8_append on the e4m3 cache), which computes each sequence's
+new slot, writes its K/V and attends in one launch, then merges; with
+``--no-append``, and always for the prefill + decode mix (pa_chunked_prefill)
+and the shared-prefix decode, the three calls pa_compute_slot_mapping,
+pa_reshape_and_cache and the attention call.  The separate calls are timed
+in every run (``cache_write``, and ``separate_calls`` beside an appending
+step).  Inputs are resident in HBM before the timed region.
 
 Workload (default 3): one Llama-3-70B attention layer in bf16 -- 128
 sequences of U[2048, 8192] tokens, 64 query / 8 KV heads, head_dim 128,
@@ -227,6 +233,12 @@ def parse():
     p.add_argument("--tp", type=int, default=1,
                    help="one tensor-parallel rank's share: H_q / tp query and H_kv / tp KV "
                         "heads of the workload (tp divides H_kv)")
+    p.add_argument("--append", action=argparse.BooleanOptionalAction, default=True,
+                   help="decode workloads: the step is one pa_decode_append (or "
+                        "pa_decode_fp8_append) call, which computes the new tokens' slots, "
+                        "writes them and attends in one launch plus the merge (default); "
+                        "--no-append times the three separate calls instead.  The separate "
+                        "calls are timed either way")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="also run one plain device copy of BYTES bytes (a reference for "
                         "hardware byte counters)")
@@ -421,13 +433,32 @@ def main():
                            wl.scale, kv_split_tokens=args.kv_split, block_refcounts=refcounts,
                            out=out, workspace=ws)
 
+    append = args.append and not chunked and not args.shared_prefix
+
+    def attention_append():
+        if fp8:
+            binding.decode_fp8_append(t["query"], t["key"], t["value"], t["k_cache8"],
+                                      t["v_cache8"], t["k_scales"], t["v_scales"], bt, lens,
+                                      wl.max_seq_len, wl.scale, block_refcounts=refcounts,
+                                      out=out, workspace=ws)
+        else:
+            binding.decode_append(t["query"], t["key"], t["value"], t["k_cache"], t["v_cache"],
+                                  bt, lens, wl.max_seq_len, wl.scale,
+                                  kv_split_tokens=args.kv_split, block_refcounts=refcounts,
+                                  out=out, workspace=ws)
+
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
 
-    def step(ev=None, sev=None, wev=None):
+    def step(ev=None, sev=None, wev=None, fused=append):
         if scratch is not None:
             scratch.fill_(1)  # evicts the Infinity Cache; outside every timed event
         if sev is not None:
             sev[0].record(stream)
+        if fused:  # slot computation, cache write and attention in one call
+            attention_append()
+            if sev is not None:
+                sev[1].record(stream)
+            return
         binding.compute_slot_mapping(bt, lens, qsl, shp.block_size, num_tokens=T, out=slots)
         if wev is not None:
             wev.record(stream)
@@ -474,23 +505,36 @@ def main():
     ms_step = ms_total / args.steps
     if args.flush:  # the flushes are not part of the step
         ms_step = sum(a.elapsed_time(b) for a, b in sevs) / args.steps
-    # The parts of the step: K more steps under the same conditions, with
-    # events around the attention call, the cache write and the slot mapping.
+    fused_ms = [a.elapsed_time(b) for a, b in sevs]  # the step is one call when appending
+    # The parts of the step: K more steps of the separate calls under the
+    # same conditions, with events around the attention call, the cache
+    # write and the slot mapping.
     evs, sevs2 = pairs(), pairs()
     wevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        step(evs[k], sevs2[k], wevs[k])
+        step(evs[k], sevs2[k], wevs[k], fused=False)
     torch.cuda.synchronize()
-    sevs = sevs2
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg = sum(attn_ms) / len(attn_ms)
-    slot_ms = [a[0].elapsed_time(w) for a, w in zip(sevs, wevs)]
+    attn_ms = sep_attn_ms = [a.elapsed_time(b) for a, b in evs]
+    slot_ms = [a[0].elapsed_time(w) for a, w in zip(sevs2, wevs)]
     write_ms = [w.elapsed_time(e[0]) for w, e in zip(wevs, evs)]
+    separate_ms = None
+    if append:
+        # the three separate calls again, with only the bracketing events
+        sevs3 = pairs()
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            step(sev=sevs3[k], fused=False)
+        torch.cuda.synchronize()
+        separate_ms = sum(a.elapsed_time(b) for a, b in sevs3) / args.steps
     call = ("pa_chunked_prefill" + ("_fp8" if fp8 else "")) if chunked else (
         "pa_decode_fp8" if fp8 else "pa_decode")
     if args.shared_prefix:
         call = "pa_decode_shared_prefix"
+    if append:  # the roofline covers the appending call, which is the whole step
+        call = "pa_decode_fp8_append" if fp8 else "pa_decode_append"
+        attn_ms = fused_ms
+    attn_avg = sum(attn_ms) / len(attn_ms)
     print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, {call} avg "
           f"{attn_avg:.4f} ms (p10 {percentile(attn_ms, 10):.4f}, median "
           f"{percentile(attn_ms, 50):.4f}, p90 {percentile(attn_ms, 90):.4f})",
@@ -514,6 +558,8 @@ def main():
             print(f"[bench] read ceiling {ceiling:.1f} GB/s ({ceiling_how})", file=sys.stderr,
                   flush=True)
     kv_bytes, call_bytes = algorithmic_bytes(wl, args.kv_dtype)
+    if append:  # the new tokens' K and V, read and written inside the call
+        call_bytes += 2 * T * shp.num_kv_heads * shp.head_dim * (e_in + e_out)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     workload_name = shp.name if not fp8 else shp.name.replace("-bf16", "-fp8kv")
     if chunked:
@@ -544,7 +590,9 @@ def main():
     else:
         achieved = call_bytes / (attn_avg * 1e-3) / 1e9
         roofline = {
-            "kernel": f"{call}: balanced split-K attention kernel + merge kernel",
+            "kernel": (f"{call}: balanced split-K attention kernel (the wave reading a "
+                       "sequence's last key step first writes its new token) + merge kernel")
+                      if append else f"{call}: balanced split-K attention kernel + merge kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
@@ -590,7 +638,9 @@ def main():
             "total_tokens": sum(wl.seq_lens),
             "kv_bytes": kv_bytes,
             "kv_split_tokens": args.kv_split,
-            "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + {call}",
+            "step": (f"{call} (slot computation, cache write and attention in one launch, "
+                     "then the merge)") if append else
+                    f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + {call}",
             "shared_prefix_blocks": prefix_blocks if args.shared_prefix else 0,
             "infinity_cache_flushed": bool(args.flush),
         },
@@ -605,6 +655,13 @@ def main():
             "slot_mapping_avg_us": round(1e3 * sum(slot_ms) / len(slot_ms), 2),
         },
     }
+    if append:
+        result["separate_calls"] = {
+            "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + "
+                    f"{'pa_decode_fp8' if fp8 else 'pa_decode'}",
+            "ms_per_step": round(separate_ms, 5),
+            "attention_avg_ms": round(sum(sep_attn_ms) / len(sep_attn_ms), 5),
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.kv_dtype)

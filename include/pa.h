@@ -79,8 +79,9 @@
  *  - dtype is passed as int32_t and the stream as void* (a hipStream_t), so
  *    this header needs no HIP header.
  *  - Added entry points: pa_compute_slot_mapping (the slot step on the
- *    device), pa_version, the e4m3 cache calls, pa_decode_shared_prefix and
- *    the whole-block copies.
+ *    device), pa_version, the e4m3 cache calls, pa_decode_shared_prefix,
+ *    the whole-block copies, and pa_decode_append / pa_decode_fp8_append
+ *    (slot computation, cache write and decode of one step in one call).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -187,6 +188,40 @@ int pa_decode(void* out, const void* query, const void* k_cache,
               int32_t num_blocks, float scale, int32_t dtype,
               int32_t kv_split_tokens, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_append -- one decode step's slot computation, cache write and
+ * attention in one call: the same results, bit for bit, as
+ * pa_compute_slot_mapping (query_start_loc NULL), pa_reshape_and_cache with
+ * those slots and pa_decode on the same arguments.  Slot computation: "High-
+ * Throughput Local LLM Infrastructure ...", section "1.2 PagedAttention
+ * Mechanics & Virtual Page Tables" (block index and offset of a logical
+ * position); cache write: same page, section "2.1 PagedAttention Memory
+ * Allocation Life-Cycle", step 4.
+ * key, value: [num_seqs, num_kv_heads, head_dim] in dtype, the new token of
+ * every sequence, written at position seq_lens[s] - 1 (slot
+ * block_tables[s][(seq_lens[s]-1) / block_size] * block_size +
+ * (seq_lens[s]-1) % block_size) of k_cache / v_cache, which the call
+ * modifies; nothing is written for a sequence whose table entry there lies
+ * outside [0, num_blocks) (a negative or out-of-range slot in
+ * pa_reshape_and_cache).  The attention then includes that token.  On the
+ * balanced decode (bf16, block_size >= 8, kv_split_tokens 0, up to 4096
+ * sequences) the writes happen inside the attention launch: the wave that
+ * reads a sequence's last key step writes its new token first.  Other
+ * shapes write them in a launch of their own before the attention.
+ * Workspace as for pa_decode (pa_decode_workspace_bytes).  Two sequences
+ * whose new tokens share a slot are undefined (PA_ERR_INDEX under
+ * PA_CHECK); key or value NULL with num_seqs > 0 is PA_ERR_NULL.
+ */
+int pa_decode_append(void* out, const void* query, const void* key,
+                     const void* value, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* block_refcounts, const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t max_seq_len,
+                     int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     float scale, int32_t dtype, int32_t kv_split_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace for pa_chunked_prefill: fp32 partials for the query-chunk rows
@@ -329,6 +364,27 @@ int pa_decode_fp8(void* out, const void* query, const void* k_cache,
                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                   int32_t num_blocks, float scale, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_fp8_append -- pa_decode_append over e4m3 pools: bf16 key/value
+ * [num_seqs, num_kv_heads, head_dim] quantised with the scales of the new
+ * token's (block, KV head) exactly as pa_reshape_and_cache_fp8 does, then
+ * pa_decode_fp8; always inside the attention launch.  Same results, bit for
+ * bit, as those calls in sequence.  Arguments and limits otherwise as for
+ * pa_decode_fp8 (workspace: pa_decode_fp8_workspace_bytes).
+ */
+int pa_decode_fp8_append(void* out, const void* query, const void* key,
+                         const void* value, void* k_cache, void* v_cache,
+                         const float* k_scales, const float* v_scales,
+                         const int32_t* block_tables,
+                         int32_t max_blocks_per_seq,
+                         const int32_t* block_refcounts,
+                         const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t max_seq_len, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, float scale,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * Workspace for pa_chunked_prefill_fp8: that of pa_chunked_prefill plus the

@@ -66,6 +66,12 @@ SIGNATURES = {
     "pa_chunked_prefill_fp8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                               _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _i32, ctypes.c_int64, _f32, _vp, _sz, _vp]),
+    "pa_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                        _vp, _sz, _vp]),
+    "pa_decode_fp8_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                            _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _f32, _vp, _sz, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -273,6 +279,47 @@ def decode(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
+def _new_tokens(key: torch.Tensor, value: torch.Tensor, S: int, Hkv: int, D: int,
+                dtype: torch.dtype) -> None:
+    _want(key.dim() == 3 and tuple(key.shape) == (S, Hkv, D),
+          f"key must be [{S}, {Hkv}, {D}]: one new token per sequence")
+    _want(value.shape == key.shape, "value must have the shape of key")
+    _want(key.dtype == value.dtype == dtype,
+          f"key and value must be {dtype} ({key.dtype}, {value.dtype})")
+
+
+def decode_append(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                  seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                  kv_split_tokens: int = 0, block_refcounts: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """pa_decode_append: each sequence's new token (key/value [S, H_kv, D])
+    written at position seq_len - 1 of its table, then the decode; the pools
+    are modified in place."""
+    NB, Hkv, B, D = _pools(k_cache, v_cache)
+    _rows(query, out, Hkv, D)
+    _want(query.dtype == k_cache.dtype,
+          f"query and the pools must share one dtype ({query.dtype}, {k_cache.dtype})")
+    S, Hq = query.shape[0], query.shape[1]
+    _new_tokens(key, value, S, Hkv, D, k_cache.dtype)
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _workspace(workspace)
+    _same_device(query, key, value, k_cache, v_cache, block_tables, seq_lens, block_refcounts,
+                 out, workspace)
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(decode_workspace_bytes(S, Hq, D, max_seq_len, B, kv_split_tokens),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_decode_append", lib().pa_decode_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
+        max_seq_len, Hq, Hkv, D, B, NB, scale, _dtype(query), kv_split_tokens, _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out
+
+
 def decode_noalloc(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                    scale: float, out: torch.Tensor, kv_split_tokens: int = 0,
@@ -438,6 +485,38 @@ def decode_fp8(query: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
         max_seq_len, Hq, Hkv, D, B, NB, scale, _ptr(workspace), workspace.numel(),
         _stream(stream)))
+    return out
+
+
+def decode_fp8_append(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
+                      v_scales: torch.Tensor, block_tables: torch.Tensor,
+                      seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                      block_refcounts: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode_fp8_append: bf16 key/value [S, H_kv, D] quantised into the
+    e4m3 pools at position seq_len - 1, then the e4m3 decode."""
+    NB, Hkv, B, D = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    if query.dtype != torch.bfloat16:
+        raise ValueError("the fp8 decode takes a bf16 query")
+    _rows(query, out, Hkv, D)
+    S, Hq = query.shape[0], query.shape[1]
+    _new_tokens(key, value, S, Hkv, D, torch.bfloat16)
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _workspace(workspace)
+    _same_device(query, key, value, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                 block_refcounts, out, workspace)
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(decode_fp8_workspace_bytes(S, Hq, D, max_seq_len, B),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_decode_fp8_append", lib().pa_decode_fp8_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), block_tables.shape[1],
+        _ptr(block_refcounts), _ptr(seq_lens), S, max_seq_len, Hq, Hkv, D, B, NB, scale,
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -220,6 +220,29 @@ int validate_prefix(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, 
   return PA_OK;
 }
 
+// PA_CHECK for the appending decode: the slots of the new tokens (position
+// seq_len - 1 of each table) are distinct.
+int validate_append_slots(const int32_t* d_bt, int max_blocks, const int32_t* d_lens,
+                          int num_seqs, int block_size, hipStream_t st) {
+  std::vector<int32_t> bt((size_t)num_seqs * max_blocks), lens(num_seqs);
+  if (hipMemcpyAsync(bt.data(), d_bt, bt.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(lens.data(), d_lens, lens.size() * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return PA_ERR_HIP;
+  std::vector<int64_t> slots;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int pos = lens[s] - 1;
+    if (pos < 0 || pos / block_size >= max_blocks) continue;
+    const int id = bt[(size_t)s * max_blocks + pos / block_size];
+    slots.push_back((int64_t)id * block_size + pos % block_size);
+  }
+  std::sort(slots.begin(), slots.end());
+  for (size_t i = 1; i < slots.size(); ++i)
+    if (slots[i] == slots[i - 1]) return PA_ERR_INDEX;
+  return PA_OK;
+}
+
 // Blocks the tables of a (validated) batch hold.
 int table_blocks_used(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, int num_seqs,
                       int block_size, hipStream_t st, std::vector<int64_t>* out) {
@@ -250,7 +273,9 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
                      int max_query_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int block_size, int num_blocks, float scale, int dtype, int kv_split_tokens,
                      void* workspace, size_t workspace_bytes, void* stream,
-                     const Fp8Kv& f8 = Fp8Kv(), int prefix_blocks = 0) {
+                     const Fp8Kv& f8 = Fp8Kv(), int prefix_blocks = 0,
+                     bool append = false, const void* new_k = nullptr,
+                     const void* new_v = nullptr) {
   int rc = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
   if (rc != PA_OK) return rc;
   if (num_seqs < 0 || num_tokens < 0 || max_blocks <= 0 || num_blocks <= 0 ||
@@ -259,6 +284,7 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
   if (f8.kv_fp8 && (!f8.k_scales || !f8.v_scales)) return PA_ERR_NULL;
+  if (append && (!new_k || !new_v)) return PA_ERR_NULL;
   if ((int64_t)num_seqs * num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   WorkspacePlan plan;
   const bool chunk_entry = qsl != nullptr;
@@ -298,6 +324,10 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
                            block_size, st);
       if (rc != PA_OK) return rc;
     }
+    if (new_k) {
+      rc = validate_append_slots(block_tables, max_blocks, seq_lens, num_seqs, block_size, st);
+      if (rc != PA_OK) return rc;
+    }
     if (f8.kv_fp8) {
       std::vector<int64_t> used;
       rc = table_blocks_used(block_tables, max_blocks, seq_lens, num_seqs, block_size, st, &used);
@@ -331,6 +361,8 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
   a.kv_fp8 = f8.kv_fp8;
   a.k_scales = f8.k_scales;
   a.v_scales = f8.v_scales;
+  a.new_k = new_k;
+  a.new_v = new_v;
   // Piece counts per row: written by the MFMA chunk kernel only (the
   // vector-ALU path's merge derives its split count from split_tokens).
   a.row_pieces = plan.rp && mfma ? reinterpret_cast<int32_t*>(ws + plan.a_o + plan.a_ml) : nullptr;
@@ -357,7 +389,9 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     err = pa::launch_decode_streamk(a, header, st);
   } else {
     if (a.kv_fp8) return PA_ERR_UNSUPPORTED;  // the fp8 cache has the balanced decode only
-    err = pa::launch_attention(a, false, nullptr, st);
+    // paths that do not fuse the appending decode's writes get them first
+    err = new_k ? pa::launch_append_tokens(a, st) : hipSuccess;
+    if (err == hipSuccess) err = pa::launch_attention(a, false, nullptr, st);
   }
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -494,6 +528,21 @@ int pa_decode(void* out, const void* query, const void* k_cache, const void* v_c
                           block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
                           kv_split_tokens, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, float scale, int32_t dtype,
+                     int32_t kv_split_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                          dtype, kv_split_tokens, workspace, workspace_bytes, stream, Fp8Kv(), 0,
+                          true, key, value);
 }
 
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens,
@@ -722,6 +771,27 @@ int pa_decode_fp8(void* out, const void* query, const void* k_cache, const void*
                           block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                           PA_BF16, 0, workspace, workspace_bytes, stream, f8);
+}
+
+int pa_decode_fp8_append(void* out, const void* query, const void* key, const void* value,
+                         void* k_cache, void* v_cache, const float* k_scales,
+                         const float* v_scales, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (block_size > 0 && block_size < 16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxBalancedSeqs) return PA_ERR_UNSUPPORTED;
+  Fp8Kv f8;
+  f8.kv_fp8 = 1;
+  f8.k_scales = k_scales;
+  f8.v_scales = v_scales;
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                          PA_BF16, 0, workspace, workspace_bytes, stream, f8, 0, true, key,
+                          value);
 }
 
 size_t pa_chunked_prefill_fp8_workspace_bytes(int32_t num_seqs, int32_t num_tokens,

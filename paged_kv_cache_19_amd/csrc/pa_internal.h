@@ -44,6 +44,12 @@ struct AttnArgs {
   int32_t prefix_keys;
   int32_t prefix_group;
   int32_t prefix_slots;
+  // Appending decode (pa_decode_append, pa_decode_fp8_append): the new
+  // token of every sequence, key and value rows [num_seqs, Hkv, D] (the
+  // pool dtype; bf16 for an e4m3 pool), written at position seq_len - 1
+  // before the attention reads it.  nullptr: nothing is written.
+  const void* new_k;
+  const void* new_v;
 };
 
 // 16-row MFMA tiles of query rows per shared-prefix item: a group holds
@@ -92,6 +98,11 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int32_t num_tokens, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                         hipStream_t stream);
+
+// The appending decode's cache writes on their own (a.new_k / a.new_v, one
+// new token per sequence at position seq_len - 1; a.kv_fp8 selects the
+// quantising write), for the attention paths that do not fuse them.
+hipError_t launch_append_tokens(const AttnArgs& a, hipStream_t stream);
 
 // Split-K attention pass (writes final rows for single-split rows and
 // partials otherwise), then the log-sum-exp merge pass when needed.

@@ -63,6 +63,11 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their "no wait" maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -284,6 +289,76 @@ __global__ __launch_bounds__(2 * D) void reshape_and_cache_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Appending decode: the new token of sequence s (row t of new_k / new_v) goes
+// to position L - 1 of its table, slot table[s][(L-1) / B] * B + (L-1) mod B,
+// the slot slot_mapping_kernel gives that position.  The bits written are
+// those of reshape_and_cache_kernel (a copy) or, for an e4m3 pool, of
+// reshape_and_cache_fp8_kernel (the same division, clamp and RNE
+// conversion, element by element).  Nothing is written where the table
+// cannot address the position or names a block outside the pool, as with a
+// negative or out-of-range slot there.  One wave, D / 64 elements per lane;
+// with WAIT it returns with the wave's stores complete, so whatever the
+// wave loads next sees them.
+// ---------------------------------------------------------------------------
+template <int ES, int D, bool FP8, bool WAIT>
+__device__ __forceinline__ void append_token(const AttnArgs& a, int s, int kvh, int L, int t) {
+  constexpr int PER = D / 64;  // elements per lane
+  static_assert(PER == 1 || PER == 2, "head_dim 64 or 128");
+  const int lane = threadIdx.x & 63;
+  const int lg = a.log2_block;
+  const int pos = L - 1;
+  if (pos < 0 || (pos >> lg) >= a.max_blocks) return;
+  const int id = a.block_tables[(int64_t)s * a.max_blocks + (pos >> lg)];
+  if (id < 0 || id >= a.num_blocks) return;
+  const int B = 1 << lg;
+  const int off = pos & (B - 1);
+  const int64_t hb = (int64_t)id * a.num_kv_heads + kvh;  // (block, KV head)
+  const int64_t src = ((int64_t)t * a.num_kv_heads + kvh) * D + PER * lane;
+  const int64_t kdst = (hb * B + off) * D + PER * lane;   // K row of the slot
+  const int64_t vdst = (hb * D + PER * lane) * B + off;   // V column entries, stride B
+  if constexpr (FP8) {
+    const uint16_t* nk = static_cast<const uint16_t*>(a.new_k) + src;
+    const uint16_t* nv = static_cast<const uint16_t*>(a.new_v) + src;
+    const float ks = a.k_scales[hb], vs = a.v_scales[hb];
+    float xk[2] = {0.f, 0.f}, xv[2] = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      xk[e] = sat_e4m3(__fdiv_rn(__uint_as_float((uint32_t)nk[e] << 16), ks));
+      xv[e] = sat_e4m3(__fdiv_rn(__uint_as_float((uint32_t)nv[e] << 16), vs));
+    }
+    const uint32_t ck = __builtin_amdgcn_cvt_pk_fp8_f32(xk[0], xk[1], 0, false);
+    const uint32_t cv = __builtin_amdgcn_cvt_pk_fp8_f32(xv[0], xv[1], 0, false);
+    uint8_t* kc = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+    uint8_t* vc = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+    if constexpr (PER == 2) *reinterpret_cast<uint16_t*>(kc + kdst) = (uint16_t)(ck & 0xFFFF);
+    else kc[kdst] = (uint8_t)(ck & 0xFF);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) vc[vdst + (int64_t)e * B] = (uint8_t)((cv >> (8 * e)) & 0xFF);
+  } else {
+    typedef typename std::conditional<ES == 2, uint16_t, uint32_t>::type E;
+    const E* nk = static_cast<const E*>(a.new_k) + src;
+    const E* nv = static_cast<const E*>(a.new_v) + src;
+    E* kc = static_cast<E*>(const_cast<void*>(a.k_cache));
+    E* vc = static_cast<E*>(const_cast<void*>(a.v_cache));
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      kc[kdst + e] = nk[e];
+      vc[vdst + (int64_t)e * B] = nv[e];
+    }
+  }
+  if constexpr (WAIT) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stores count in vmcnt here
+}
+
+// The appending decode's writes on their own, before an attention path that
+// does not fuse them (fixed splits, the vector-ALU kernel): one wave per
+// (sequence, KV head).
+template <int ES, int D, bool FP8>
+__global__ __launch_bounds__(64) void append_tokens_kernel(AttnArgs a) {
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  append_token<ES, D, FP8, false>(a, s, kvh, a.seq_lens[s], s);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 attention on MFMA.
 //
 // One wave serves one (sequence, KV head, row-tile group, context split).
@@ -323,6 +398,23 @@ __device__ __forceinline__ float xl_sum(float v) {
 template <int D>
 struct KVFrag {
   bf16x8 ka[D / 32], kb[D / 32], v[D / 16];
+};
+
+// An appending decode's new token as the bf16 decode's fragments hold it:
+// in the step whose first key is c it is token u = (L - 1) - c.  Its K row
+// sits in the "a" (u % 8 < 4) or "b" fragments of the lanes with
+// l % 16 == i (the row of MFMA "a"/"b" that is token u), dims 8 * (l / 16)
+// + 32 * kk; its V entries in element u % 8 of the V fragments of the lanes
+// with l / 16 == u / 8 (head_dim l % 16 + 16 * n).  Each lane holds its own
+// share, loaded from the call's key / value rows.
+template <int D>
+struct NewToken {
+  int c;              // first key of the step holding the token (-1: none)
+  bool ka, kb;        // this lane's "a" / "b" K fragments hold the token
+  int vd;             // dword of the V fragments holding element u % 8
+  uint32_t vmask;     // its bits of the token in this lane (0: none)
+  u32x4 k[D / 32];    // the lane's K dims of the token
+  uint32_t v[D / 16]; // the lane's V entries, in place within dword vd
 };
 
 // Rescaling of the running output is skipped while a chunk's maximum stays
@@ -442,9 +534,10 @@ __device__ __forceinline__ int leading_shared_keys(const AttnArgs& a, const SeqV
 // Cache policy: with STREAM every K/V load is non-temporal (private blocks
 // are read once per call); without it loads go through the caches (shared
 // prefix blocks, and query chunks whose K/V several waves re-read).
-template <int D, int R, bool STREAM, int NSETS = 2>
+template <int D, int R, bool STREAM, int NSETS = 2, bool PATCH = false>
 __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int kv_wave, int kv_min,
-                                       int k_begin, int k_end, RowState<D, R>& st) {
+                                       int k_begin, int k_end, RowState<D, R>& st,
+                                       const NewToken<D>* nt = nullptr) {
   constexpr int KK = D / 32;
   constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -492,6 +585,26 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
 
   auto compute = [&](KVFrag<D>& f, int c) {
     const int pv_ = c + 8 * j4;
+    if constexpr (PATCH) {
+      // the step holding an appending call's new token: its K/V come from
+      // the call's key / value rows, not from the slot (written later)
+      if (c == nt->c) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 x = __builtin_bit_cast(bf16x8, nt->k[kk]);
+          f.ka[kk] = nt->ka ? x : f.ka[kk];
+          f.kb[kk] = nt->kb ? x : f.kb[kk];
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          u32x4 x = __builtin_bit_cast(u32x4, f.v[n]);
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            x[d] = d == nt->vd ? ((x[d] & ~nt->vmask) | nt->v[n]) : x[d];
+          f.v[n] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+    }
     if (c + 32 > kv_wave) {
       // Keys past the last visible one may be unwritten slots: zero their V
       // so that 0-weight * garbage cannot produce NaN.
@@ -602,6 +715,21 @@ struct KVFrag8 {
   float ks, vs;        // scales of the block of the lane's 16 tokens
 };
 
+// An appending e4m3 decode's new token as attend_fp8's fragments hold it:
+// token u of its 64-key step sits in K fragment x = (u / 4) % 4 of the
+// lanes with l % 16 == 4 * (u / 16) + u % 4 (bytes (D/4) * (l/16) + ...),
+// and in byte u % 4 of dword (u % 16) / 4 of the V fragments of the lanes
+// with l / 16 == u / 16.  Its codes, those the cache write gives it, wait
+// in LDS (K row, then V column, D bytes each, head_dim order): held in
+// registers across the step loop they would not fit beside the ring.
+struct NewToken8 {
+  int c;                 // first key of the step holding the token (-1: none)
+  int kx;                // K fragment holding it
+  int vd, sh;            // dword and bit offset of its V byte
+  bool k_sel, v_sel;     // this lane holds its K bytes / a V byte of it
+  const uint8_t* codes;  // LDS: K codes [D], then V codes [D]
+};
+
 // Eight e4m3 codes (two dwords, lowest byte first) as bf16, exactly: gfx950
 // converts a pair of fp8 codes straight to a pair of bf16 (with a unit
 // scale the result is the code's value; every e4m3 value is a bf16 value).
@@ -629,10 +757,11 @@ __device__ __forceinline__ u32x4 load_u32x4(const uint8_t* p) {
 constexpr int kDecodeSets = 3;
 constexpr int kFp8Sets = 3;
 
-template <int D, bool STREAM, int R = 1, int NSETS = kFp8Sets>
+template <int D, bool STREAM, int R = 1, int NSETS = kFp8Sets, bool PATCH = false>
 __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, int kv_wave,
                                            int kv_min, int k_begin, int k_end,
-                                           RowState<D, R>& st) {
+                                           RowState<D, R>& st,
+                                           const NewToken8* nt = nullptr) {
   constexpr int KK = D / 32;
   constexpr int KP = D / 64;
   constexpr int NT = D / 16;
@@ -687,6 +816,28 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
   // last step of a piece can; the tests sit behind a wave-uniform branch.
   auto compute = [&](KVFrag8<D>& f, int c, bool mask) {
     const int pv = c + 16 * j4;
+    if constexpr (PATCH) {
+      // the step holding an appending call's new token: its codes come from
+      // registers, not from the slot (written after the share)
+      if (c == nt->c) {
+        u32x4 kc[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p)
+          kc[p] = *reinterpret_cast<const u32x4*>(nt->codes + (D / 4) * j4 + 16 * p);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int p = 0; p < KP; ++p) f.k[x][p] = nt->k_sel && x == nt->kx ? kc[p] : f.k[x][p];
+        const uint32_t vmask = nt->v_sel ? 0xFFu << nt->sh : 0u;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint32_t code = (uint32_t)nt->codes[D + i + 16 * n] << nt->sh;
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            f.v[n][d] = d == nt->vd ? ((f.v[n][d] & ~vmask) | (code & vmask)) : f.v[n][d];
+        }
+      }
+    }
     if (mask) {
       rare_branch();
       // zero the V bytes of keys >= kv_wave (16 keys per lane, 4 per dword)
@@ -992,9 +1143,15 @@ __device__ __forceinline__ void decode_prefix_scan(int* P, int S, int lane) {
 // PREFIX: the shared-prefix work list (prefix items after the sequences'
 // own items); an instantiation without it holds no prefix path, so the
 // plain decode keeps its register budget.
-template <int D, bool FP8, int NSETS, bool PREFIX = false>
+// APPEND: the appending decode.  The wave whose piece holds an item's last
+// step writes the sequence's new token for that KV head before it loads
+// anything of the piece: that step is the only one that reads the slot, so
+// no other wave waits for the write.  A separate instantiation, so that the
+// plain decode's K/V stay read-only to the compiler.
+template <int D, bool FP8, int NSETS, bool PREFIX = false, bool APPEND = false>
 __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, const int* Ls,
-                                             int64_t N, int64_t weff, int w) {
+                                             int64_t N, int64_t weff, int w,
+                                             uint8_t* tok_lds = nullptr) {
   constexpr int STEP = FP8 ? 64 : 32;
   const int S = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);  // work-list entries
   const int Hkv = a.num_kv_heads;
@@ -1011,6 +1168,7 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     }
     s = lo;
   }
+  const int s_first = s;
   while (g < g_end) {
     while ((int64_t)Hkv * P[s + 1] <= g) ++s;
     const int cost = P[s + 1] - P[s];  // steps + kPieceCostSteps
@@ -1057,6 +1215,80 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     seq_rows(a.query_start_loc, s, a.num_tokens, r0, qn);
     const SeqView v = seq_view(a, s, kvh, Ls[s], r0, 1);
     const int kl = min(v.L, v.kcap);
+    // Appending: the step that holds the new token takes its K/V from the
+    // call's rows in registers; the cache write comes after the share (below).
+    NewToken<D> nt;
+    NewToken8 nt8;
+    nt.c = -1;
+    nt8.c = -1;
+    const int new_pos = Ls[s] - 1;
+    const int new_id = APPEND && c1 == nch && new_pos >= 0 && new_pos < kl
+                           ? a.block_tables[(int64_t)s * a.max_blocks + (new_pos >> a.log2_block)]
+                           : -1;
+    if constexpr (APPEND && FP8) {
+      if (new_id >= 0 && new_id < a.num_blocks) {  // exactly when the write happens
+        const int lane = threadIdx.x & 63;
+        const int u = new_pos & 63;                 // the token within its 64-key step
+        nt8.c = new_pos - u;
+        nt8.kx = (u >> 2) & 3;
+        nt8.k_sel = (lane & 15) == 4 * (u >> 4) + (u & 3);
+        nt8.v_sel = (lane >> 4) == (u >> 4);
+        nt8.vd = (u & 15) >> 2;
+        nt8.sh = 8 * (u & 3);
+        nt8.codes = tok_lds;
+        // codes as the cache write makes them (x / scale rounded once,
+        // clamped to +-448, e4m3 with round to nearest even); lane l makes
+        // those of dims D/64 * l .. of the K row and the V column
+        constexpr int PER = D / 64;
+        const int64_t hb = (int64_t)new_id * Hkv + kvh;
+        const float ks = a.k_scales[hb], vs = a.v_scales[hb];
+        const int64_t src = ((int64_t)r0 * Hkv + kvh) * D + PER * lane;
+        const uint16_t* nk = static_cast<const uint16_t*>(a.new_k) + src;
+        const uint16_t* nv = static_cast<const uint16_t*>(a.new_v) + src;
+        float xk[2] = {0.f, 0.f}, xv[2] = {0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          xk[e] = sat_e4m3(__fdiv_rn(__uint_as_float((uint32_t)nk[e] << 16), ks));
+          xv[e] = sat_e4m3(__fdiv_rn(__uint_as_float((uint32_t)nv[e] << 16), vs));
+        }
+        const uint32_t ck = __builtin_amdgcn_cvt_pk_fp8_f32(xk[0], xk[1], 0, false);
+        const uint32_t cv = __builtin_amdgcn_cvt_pk_fp8_f32(xv[0], xv[1], 0, false);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          tok_lds[PER * lane + e] = (uint8_t)(ck >> (8 * e));
+          tok_lds[D + PER * lane + e] = (uint8_t)(cv >> (8 * e));
+        }
+      }
+    }
+    if constexpr (APPEND && !FP8) {
+      const int pos = new_pos;
+      const int id = new_id;
+      if (id >= 0 && id < a.num_blocks) {  // exactly when the write happens
+        const int lane = threadIdx.x & 63;
+        const int u = pos & 31;                  // the token within its step
+        const bool b = (u & 4) != 0;             // "b" rows are the "a" tokens + 4
+        const int ua = b ? u - 4 : u;
+        const bool krow = (lane & 15) == 4 * (ua >> 3) + (ua & 3);
+        const bool vcol = (lane >> 4) == (u >> 3);
+        nt.c = pos - u;
+        nt.ka = krow && !b;
+        nt.kb = krow && b;
+        nt.vd = (u & 7) >> 1;
+        const int sh = 16 * (u & 1);
+        nt.vmask = vcol ? 0xFFFFu << sh : 0u;
+        const int64_t row = ((int64_t)r0 * Hkv + kvh) * D;
+        const uint16_t* nk = static_cast<const uint16_t*>(a.new_k) + row;
+        const uint16_t* nv = static_cast<const uint16_t*>(a.new_v) + row;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          nt.k[kk] = krow ? __builtin_bit_cast(u32x4, load_bf16x8(nk + 8 * (lane >> 4) + 32 * kk))
+                          : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n)
+          nt.v[n] = vcol ? (uint32_t)nv[(lane & 15) + 16 * n] << sh : 0u;
+      }
+    }
+    constexpr bool PATCH = APPEND && !FP8;
     RowState<D, 1> st;
     load_rows<D, 1, FP8>(a, v, 0, st);
     const int kb0 = a.prefix_keys;  // step 0 of an own item starts after the shared prefix
@@ -1069,14 +1301,16 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
                      : k_begin < (64 << a.log2_block) ? leading_shared_keys(a, v) & ~(STEP - 1)
                                                       : 0;
     if constexpr (FP8) {
-      if (k_sh > k_begin) attend_fp8<D, false, 1, NSETS>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+      constexpr bool PATCH8 = APPEND;
+      if (k_sh > k_begin)
+        attend_fp8<D, false, 1, NSETS, PATCH8>(a, v, kl, kl, k_begin, min(k_sh, k_end), st, &nt8);
       if (k_end > max(k_begin, k_sh))
-        attend_fp8<D, true, 1, NSETS>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+        attend_fp8<D, true, 1, NSETS, PATCH8>(a, v, kl, kl, max(k_begin, k_sh), k_end, st, &nt8);
     } else {
       if (k_sh > k_begin)
-        attend<D, 1, false, NSETS>(a, v, kl, kl, k_begin, min(k_sh, k_end), st);
+        attend<D, 1, false, NSETS, PATCH>(a, v, kl, kl, k_begin, min(k_sh, k_end), st, &nt);
       if (k_end > max(k_begin, k_sh))
-        attend<D, 1, true, NSETS>(a, v, kl, kl, max(k_begin, k_sh), k_end, st);
+        attend<D, 1, true, NSETS, PATCH>(a, v, kl, kl, max(k_begin, k_sh), k_end, st, &nt);
     }
     if (a.prefix_keys > 0) {
       // every row is merged with its prefix part: own pieces in slots
@@ -1089,10 +1323,33 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
                        PartialDst{a.sk_part_o, a.sk_part_ml, a.sk_slots, (int64_t)s * a.num_q_heads});
     }
   }
+  if constexpr (APPEND) {
+    // The cache writes of the new tokens whose last step this share held,
+    // once its attention is done: stores issued while every wave streams
+    // K/V would hold up the wave's next loads until they complete.  The
+    // same walk over the share's items as above.
+    int64_t g2 = (int64_t)w * N / weff;
+    int s2 = s_first;
+    while (g2 < g_end) {
+      while ((int64_t)Hkv * P[s2 + 1] <= g2) ++s2;
+      const int cost = P[s2 + 1] - P[s2];
+      const int nch = cost - kPieceCostSteps;
+      const int64_t base = (int64_t)Hkv * P[s2];
+      const int kvh = (int)((g2 - base) / cost);
+      const int64_t g_item = base + (int64_t)kvh * cost + kPieceCostSteps;
+      const int c0 = (int)max((int64_t)0, g2 - g_item);
+      const int c1 = (int)min((int64_t)nch, g_end - g_item);
+      g2 = g_item + nch;
+      if (c1 <= c0 || c1 != nch) continue;
+      int r0, qn;
+      seq_rows(a.query_start_loc, s2, a.num_tokens, r0, qn);
+      append_token<2, D, FP8, false>(a, s2, kvh, Ls[s2], r0);
+    }
+  }
 }
 
 
-template <int D, bool FP8, bool PREFIX = false>
+template <int D, bool FP8, bool PREFIX = false, bool APPEND = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2, (FP8 ? kFp8Sets : kDecodeSets) > 2 ? 1 : 2)))
 void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
@@ -1122,7 +1379,10 @@ void decode_streamk_kernel(AttnArgs a, int waves, StreamKHeader* hdr) {
   // the block table and of the fp8 scales.  A bijection of [0, weff).
   const int nb = (int)weff, xq = nb >> 3, xr = nb & 7, xk = blockIdx.x & 7;
   const int w = xk * xq + min(xk, xr) + (blockIdx.x >> 3);
-  decode_share<D, FP8, FP8 ? kFp8Sets : kDecodeSets, PREFIX>(a, P, Ls, N, weff, w);
+  // appending e4m3 decode: the new token's codes (K row, V column) after Ls
+  uint8_t* tok_lds = reinterpret_cast<uint8_t*>(smem + ((2 * S + 1 + 3) & ~3));
+  decode_share<D, FP8, FP8 ? kFp8Sets : kDecodeSets, PREFIX, APPEND>(a, P, Ls, N, weff, w,
+                                                                      tok_lds);
 }
 
 // Up to kMergeBatch pieces of one row held in registers, so that all of
@@ -1315,10 +1575,6 @@ struct PrefillShape {
 constexpr int kPrefillGroup = 4;                        // steps between barriers
 constexpr int kPrefillStages = 2 * kPrefillGroup + 1;   // LDS ring of K/V steps
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
-// left at their "no wait" maxima).
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // global_load_lds of 16 bytes: lane l's bytes land at lds_base + 16 * l.
 __device__ __forceinline__ void load_to_lds(const void* src, void* lds_base) {
@@ -2189,16 +2445,23 @@ hipError_t resident(Residency& c, K kernel, int threads, size_t lds, int seqs, i
 
 template <int D, bool FP8 = false>
 hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
-  static thread_local Residency cache, cache_p;
+  static thread_local Residency cache, cache_p, cache_a;
   const int entries = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);
-  const size_t lds = (size_t)(2 * entries + 1) * sizeof(int);
-  int waves = 0;
   const bool prefix = a.prefix_keys > 0;
-  hipError_t err = prefix ? resident(cache_p, decode_streamk_kernel<D, FP8, true>, 64, lds, entries, waves)
-                          : resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, entries, waves);
+  const bool append = a.new_k != nullptr;  // never together with a prefix (host)
+  // P and Ls, then (appending e4m3 decode) the new token's 2 * D codes at a
+  // 16-byte boundary
+  const size_t lds = append && FP8 ? (size_t)((2 * entries + 1 + 3) & ~3) * sizeof(int) + 2 * D
+                                   : (size_t)(2 * entries + 1) * sizeof(int);
+  int waves = 0;
+  hipError_t err =
+      prefix ? resident(cache_p, decode_streamk_kernel<D, FP8, true>, 64, lds, entries, waves)
+      : append ? resident(cache_a, decode_streamk_kernel<D, FP8, false, true>, 64, lds, entries, waves)
+               : resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, entries, waves);
   if (err != hipSuccess) return err;
   StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
   if (prefix) decode_streamk_kernel<D, FP8, true><<<waves, 64, lds, st>>>(a, waves, hdr);
+  else if (append) decode_streamk_kernel<D, FP8, false, true><<<waves, 64, lds, st>>>(a, waves, hdr);
   else decode_streamk_kernel<D, FP8><<<waves, 64, lds, st>>>(a, waves, hdr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -2506,6 +2769,23 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   else if (elem_bytes == 4 && head_dim == 128) PA_RC(4, 128);
   else PA_RC(4, 64);
 #undef PA_RC
+  return hipGetLastError();
+}
+
+hipError_t launch_append_tokens(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_seqs, a.num_kv_heads);
+#define PA_AT(ES, D, F8) append_tokens_kernel<ES, D, F8><<<grid, 64, 0, stream>>>(a)
+  if (a.kv_fp8) {
+    if (a.head_dim == 128) PA_AT(2, 128, true);
+    else PA_AT(2, 64, true);
+  } else if (a.bf16) {
+    if (a.head_dim == 128) PA_AT(2, 128, false);
+    else PA_AT(2, 64, false);
+  } else {
+    if (a.head_dim == 128) PA_AT(4, 128, false);
+    else PA_AT(4, 64, false);
+  }
+#undef PA_AT
   return hipGetLastError();
 }
 

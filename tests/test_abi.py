@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 28, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding.SIGNATURES)
@@ -149,6 +149,44 @@ def test_other_entry_points_reject_bad_arguments(lib):
     f8args[20] = (1 << 27) - 1
     f8args[23] = 16
     assert f8(*f8args) == -5
+
+
+def _append(lib, fp8=False, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE,
+             maxb=4, lens=FAKE, S=2, maxlen=64, Hq=8, Hkv=2, D=128, B=16, NB=8, scale=0.1,
+             dtype=1, split=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    if fp8:
+        return lib.pa_decode_fp8_append(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"],
+                                        a["ks"], a["vs"], a["bt"], a["maxb"], None, a["lens"],
+                                        a["S"], a["maxlen"], a["Hq"], a["Hkv"], a["D"], a["B"],
+                                        a["NB"], a["scale"], a["ws"], a["wsb"], None)
+    return lib.pa_decode_append(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"],
+                                a["maxb"], None, a["lens"], a["S"], a["maxlen"], a["Hq"],
+                                a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], a["dtype"],
+                                a["split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1), (dict(kc=None), -1),
+    (dict(bt=None), -1), (dict(Hq=6, Hkv=4), -2), (dict(D=96), -4), (dict(B=128), -4),
+    (dict(scale=0.0), -2), (dict(ws=None), -5), (dict(wsb=16), -5),
+])
+def test_appending_decode_rejects_bad_arguments(lib, fp8, kw, code):
+    """pa_decode_append / pa_decode_fp8_append check their arguments like
+    pa_decode / pa_decode_fp8, and need both new-token arrays."""
+    assert _append(lib, fp8=fp8, **kw) == code
+
+
+def test_appending_decode_limits_and_empty_batch(lib):
+    assert _append(lib, S=0, k=None, v=None, out=None) == 0
+    assert _append(lib, fp8=True, S=0, k=None, v=None, out=None) == 0
+    assert _append(lib, fp8=True, ks=None) == -1
+    assert _append(lib, fp8=True, B=8) == -4       # e4m3 pools need block_size >= 16
+    assert _append(lib, fp8=True, S=5000) == -4    # the e4m3 decode stops at 4,096
+    assert _append(lib, dtype=7) == -3
+    assert _append(lib, split=96) == -2
 
 
 def _shared(lib, **kw):

@@ -3,7 +3,7 @@ what they are meant to: both head_dims on every path, both kinds of batch,
 odd group sizes, and an oracle cost within the cap.  CPU only."""
 from tests.test_gpu_fuzz import MAX_ORACLE_MACS, N_CASES, draw, draw_shared
 
-KINDS = ("bf16", "f32", "fp8", "fp8chunk")
+KINDS = ("bf16", "f32", "fp8", "fp8chunk", "append", "append8")
 
 
 def test_fuzz_draws_are_reproducible():
@@ -30,6 +30,8 @@ def test_fuzz_draws_cover_the_shapes():
     assert ("bf16", "chunked", True) in seen and ("bf16", "chunked", False) in seen
     assert ("f32", "chunked", True) in seen and ("f32", "chunked", False) in seen
     assert ("fp8", "chunked", True) not in seen            # e4m3 decode: single-token rows
+    assert ("append", "chunked", True) not in seen         # appending decode: one new token
+    assert ("append8", "chunked", True) not in seen
     assert ("fp8chunk", "chunked", False) not in seen      # every e4m3 chunked case has a chunk
     assert ("G odd", True) in seen
     for B in (8, 16, 32, 64):

@@ -1,0 +1,196 @@
+"""GPU parity of the appending decode (pa_decode_append, pa_decode_fp8_append):
+slot computation, cache write and decode of one step in one call.
+
+Each case runs the three separate calls (pa_compute_slot_mapping,
+pa_reshape_and_cache[_fp8], pa_decode[_fp8]) on one copy of the pools and
+the appending call on another.  The pools must end bit-identical (every
+slot), the outputs bit-identical (the same attention kernels read the same
+values), and the output within the bf16 bar (1e-4 for fp32) of the oracle
+over every row.  Every slot outside the cached context -- the new tokens'
+slots included -- is poisoned first (NaN, or the e4m3 NaN code), so an
+attention step that read a new token's slot before its write landed gives
+a non-finite or different output.
+
+The fused path (the write made by the wave that reads the sequence's last
+key step) serves the balanced decode; fixed splits, the vector-ALU kernel
+(fp32, or bf16 with blocks under 8 tokens) take the separate write launch.
+"""
+import pytest
+import torch
+
+import oracle.fp8 as ref8
+import oracle.paged_attention as ref
+from paged_kv_cache_19_amd import binding, workloads
+from tests.gpu_common import TOL, bits, context_mask, log, poison
+
+pytestmark = pytest.mark.gpu
+
+
+def _append_case(wl, kv_split_tokens=0):
+    t = wl.tensors
+    dev = wl.device
+    B = wl.shape.block_size
+    poison(wl)
+    bt = wl.block_tables_tensor(dev)
+    lens = wl.seq_lens_tensor(dev)
+    rc = wl.block_refcounts_tensor(dev)
+    kc0, vc0 = t["k_cache"].clone(), t["v_cache"].clone()
+
+    slots = binding.compute_slot_mapping(bt, lens, None, B)
+    binding.reshape_and_cache(t["key"], t["value"], t["k_cache"], t["v_cache"], slots)
+    want = binding.decode(t["query"], t["k_cache"], t["v_cache"], bt, lens, wl.max_seq_len,
+                          wl.scale, kv_split_tokens=kv_split_tokens, block_refcounts=rc)
+    kc1, vc1 = kc0.clone(), vc0.clone()
+    got = binding.decode_append(t["query"], t["key"], t["value"], kc1, vc1, bt, lens,
+                                wl.max_seq_len, wl.scale, kv_split_tokens=kv_split_tokens,
+                                block_refcounts=rc)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(kc1.cpu()), bits(t["k_cache"].cpu())), "K pools differ"
+    assert torch.equal(bits(vc1.cpu()), bits(t["v_cache"].cpu())), "V pools differ"
+    got_c = got.cpu()
+    assert torch.isfinite(got_c.float()).all(), "non-finite output (a poisoned slot was read)"
+    assert torch.equal(bits(got_c), bits(want.cpu())), "output differs from the separate calls"
+
+    slots_ref = ref.compute_slot_mapping(bt.cpu(), wl.seq_lens, None, B)
+    kc_ref, vc_ref = ref.reshape_and_cache(kc0.cpu(), vc0.cpu(), t["key"].cpu(),
+                                           t["value"].cpu(), slots_ref)
+    assert torch.equal(bits(kc1.cpu()), bits(kc_ref)), "K pool differs from the oracle"
+    assert torch.equal(bits(vc1.cpu()), bits(vc_ref)), "V pool differs from the oracle"
+    expect = ref.decode(t["query"].cpu(), kc_ref, vc_ref, bt.cpu(), wl.seq_lens, wl.scale)
+    return (got_c.double() - expect).abs().max().item()
+
+
+def _shape(name, Hq, Hkv, D, B, dtype=workloads.BF16):
+    return workloads.Shape(name, dtype, Hq, Hkv, D, B)
+
+
+BF16_CASES = {
+    # name: (make_workload kwargs, kv_split_tokens)
+    "llama3-8b-layer": (dict(cfg=2), 0),
+    "llama3-70b-layer": (dict(cfg=3), 0),
+    "70b-layer-b32": (dict(cfg=7), 0),
+    "block64-ragged": (dict(cfg=2, seed=51, seq_lens=[1, 2, 63, 64, 65, 129, 4000, 31],
+                            shape=_shape("b64", 32, 8, 128, 64)), 0),
+    "block8-d64": (dict(cfg=2, seed=52, seq_lens=[1, 8, 9, 300, 1023, 17, 2048],
+                        shape=_shape("b8-d64", 16, 4, 64, 8)), 0),
+    "g1-block16": (dict(cfg=2, seed=53, seq_lens=[16, 17, 33, 1000, 5],
+                        shape=_shape("g1", 8, 8, 128, 16)), 0),
+    "g16-block32": (dict(cfg=2, seed=54, seq_lens=[32, 33, 2500, 1, 96],
+                         shape=_shape("g16", 32, 2, 128, 32)), 0),
+    "fixed-splits": (dict(cfg=2, seed=55, seq_lens=[1, 257, 3000, 512, 77]), 256),
+    "block4-valu": (dict(cfg=2, seed=56, seq_lens=[1, 4, 5, 900, 63],
+                         shape=_shape("b4", 8, 2, 64, 4)), 0),
+    "tiny-fp32": (dict(cfg=1), 0),
+    "tiny-fp32-fixed-splits": (dict(cfg=1), 64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BF16_CASES))
+def test_append_matches_separate_calls_and_oracle(name):
+    kw, split = BF16_CASES[name]
+    kw = dict(kw)
+    wl = workloads.make_workload(kw.pop("cfg"), device="cuda", **kw)
+    log(f"[append] {name}: {wl.num_seqs} sequences, B={wl.shape.block_size}, "
+        f"D={wl.shape.head_dim}, G={wl.shape.num_q_heads // wl.shape.num_kv_heads}, "
+        f"{wl.shape.dtype}, split {split}")
+    err = _append_case(wl, split)
+    log(f"[append] {name}: max abs err vs oracle {err:.3e}")
+    assert err <= TOL[wl.shape.dtype]
+
+
+def test_append_twice_in_a_row():
+    """Two appending steps on one batch: the second step's tokens land one
+    position further (seq_lens + 1) and see the first step's token."""
+    wl = workloads.make_workload(2, seed=57, device="cuda", seq_lens=[15, 16, 31, 700, 2],
+                                 num_blocks=256)
+    t = wl.tensors
+    B = wl.shape.block_size
+    bt_rows = [row + [wl.spare_blocks[1 + s]] for s, row in enumerate(wl.block_tables)]
+    width = max(len(r) for r in bt_rows)
+    bt = torch.tensor([r + [wl.pad_block] * (width - len(r)) for r in bt_rows],
+                      dtype=torch.int32, device="cuda")
+    lens1 = wl.seq_lens_tensor("cuda")
+    lens2 = lens1 + 1
+    key2, value2 = t["key"].flip(0).contiguous(), t["value"].flip(0).contiguous()
+    kc_a, vc_a = t["k_cache"].clone(), t["v_cache"].clone()
+    kc_b, vc_b = t["k_cache"].clone(), t["v_cache"].clone()
+    outs = []
+    for lens, k, v in ((lens1, t["key"], t["value"]), (lens2, key2, value2)):
+        maxlen = int(lens.max().item())
+        got = binding.decode_append(t["query"], k, v, kc_a, vc_a, bt, lens, maxlen, wl.scale)
+        slots = binding.compute_slot_mapping(bt, lens, None, B)
+        binding.reshape_and_cache(k, v, kc_b, vc_b, slots)
+        want = binding.decode(t["query"], kc_b, vc_b, bt, lens, maxlen, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(got.cpu()), bits(want.cpu()))
+        outs.append(got.cpu())
+    assert torch.equal(bits(kc_a.cpu()), bits(kc_b.cpu()))
+    assert torch.equal(bits(vc_a.cpu()), bits(vc_b.cpu()))
+    lens2_l = [L + 1 for L in wl.seq_lens]
+    expect = ref.decode(t["query"].cpu(), kc_b.cpu(), vc_b.cpu(), bt.cpu(), lens2_l, wl.scale)
+    err = (outs[1].double() - expect).abs().max().item()
+    log(f"[append] two steps: max abs err vs oracle {err:.3e}")
+    assert err <= TOL[workloads.BF16]
+
+
+def _poison_fp8(wl):
+    mask = context_mask(wl).to(wl.device)
+    t = wl.tensors
+    t["k_cache8"].permute(0, 2, 1, 3)[~mask] = 0x7F
+    t["v_cache8"].permute(0, 3, 1, 2)[~mask] = 0x7F
+
+
+FP8_CASES = {
+    "llama3-8b-layer": dict(cfg=2),
+    "llama3-70b-layer": dict(cfg=3),
+    "70b-layer-b32": dict(cfg=7),
+    "block64-d64-ragged": dict(cfg=2, seed=61, seq_lens=[1, 64, 65, 130, 3000, 17],
+                               shape=_shape("b64-d64", 16, 4, 64, 64)),
+    "g16-block16": dict(cfg=2, seed=62, seq_lens=[16, 17, 1, 2048, 63],
+                        shape=_shape("g16", 32, 2, 128, 16)),
+}
+
+
+def _fp8_append_case(wl):
+    t = wl.tensors
+    dev = wl.device
+    B = wl.shape.block_size
+    _poison_fp8(wl)
+    bt = wl.block_tables_tensor(dev)
+    lens = wl.seq_lens_tensor(dev)
+    kc0, vc0 = t["k_cache8"].clone(), t["v_cache8"].clone()
+    ks, vs = t["k_scales"], t["v_scales"]
+    slots = binding.compute_slot_mapping(bt, lens, None, B)
+    binding.reshape_and_cache_fp8(t["key"], t["value"], t["k_cache8"], t["v_cache8"], ks, vs,
+                                  slots)
+    want = binding.decode_fp8(t["query"], t["k_cache8"], t["v_cache8"], ks, vs, bt, lens,
+                              wl.max_seq_len, wl.scale)
+    kc1, vc1 = kc0.clone(), vc0.clone()
+    got = binding.decode_fp8_append(t["query"], t["key"], t["value"], kc1, vc1, ks, vs, bt, lens,
+                                    wl.max_seq_len, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.cpu(), t["k_cache8"].cpu()), "K pools differ"
+    assert torch.equal(vc1.cpu(), t["v_cache8"].cpu()), "V pools differ"
+    got_c = got.cpu()
+    assert torch.isfinite(got_c.float()).all(), "non-finite output (a poisoned slot was read)"
+    assert torch.equal(bits(got_c), bits(want.cpu())), "output differs from the separate calls"
+
+    slots_ref = ref.compute_slot_mapping(bt.cpu(), wl.seq_lens, None, B)
+    kq, vq = ref8.reshape_and_cache_fp8(kc0.cpu(), vc0.cpu(), ks.cpu(), vs.cpu(), t["key"].cpu(),
+                                        t["value"].cpu(), slots_ref)
+    assert torch.equal(kc1.cpu(), kq), "fp8 K pool differs from the oracle"
+    assert torch.equal(vc1.cpu(), vq), "fp8 V pool differs from the oracle"
+    expect = ref8.decode_fp8(t["query"].cpu(), kq, vq, ks.cpu(), vs.cpu(), bt.cpu(),
+                             wl.seq_lens, wl.scale)
+    return (got_c.double() - expect).abs().max().item()
+
+
+@pytest.mark.parametrize("name", sorted(FP8_CASES))
+def test_fp8_append_matches_separate_calls_and_oracle(name):
+    kw = dict(FP8_CASES[name])
+    wl = workloads.make_workload(kw.pop("cfg"), device="cuda", kv_fp8=True, **kw)
+    log(f"[append fp8] {name}: {wl.num_seqs} sequences, B={wl.shape.block_size}, "
+        f"D={wl.shape.head_dim}")
+    err = _fp8_append_case(wl)
+    log(f"[append fp8] {name}: max abs err vs oracle {err:.3e}")
+    assert err <= TOL[workloads.BF16]

@@ -13,6 +13,7 @@ import pytest
 
 from paged_kv_cache_19_amd import workloads
 from tests.gpu_common import TOL, log, run_and_compare
+from tests.test_gpu_append import _append_case, _fp8_append_case
 from tests.test_gpu_fp8 import TOL as TOL8
 from tests.test_gpu_fp8 import _run_fp8, _run_fp8_chunked
 from tests.test_gpu_shared_prefix import TOL as TOL_SP
@@ -26,14 +27,15 @@ MAX_ORACLE_MACS = 1.5e9   # sum over query rows and heads of seq_len * head_dim
 
 def draw(kind: str, i: int):
     """(Hq, Hkv, D, B, seq_lens, q_lens) of case i of one kind."""
-    rng = random.Random({"bf16": 1000, "f32": 2000, "fp8": 3000, "fp8chunk": 4000}[kind] + i)
+    rng = random.Random({"bf16": 1000, "f32": 2000, "fp8": 3000, "fp8chunk": 4000,
+                         "append": 7000, "append8": 8000}[kind] + i)
     while True:
         Hkv = rng.choice([1, 2, 4, 8])
         G = rng.choice([g for g in (1, 2, 3, 4, 5, 8, 16) if Hkv * g <= 32])
         D = rng.choice([64, 128])
         if kind == "f32":
             B = rng.choice([1, 2, 4, 8, 16])
-        elif kind == "bf16":
+        elif kind in ("bf16", "append"):
             B = rng.choice([8, 16, 32, 64])
         else:
             B = rng.choice([16, 32, 64])
@@ -125,3 +127,21 @@ def test_fuzz_shared_prefix(i, fp8):
     _, err, diff = _run_shared(wl, prefix // B, fp8=fp8)
     log(f"[fuzz shared {i}] max abs err {err:.3e}, vs plain decode {diff:.3e}")
     assert err <= TOL_SP and diff <= TOL_SP
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"append-{i}" for i in range(N_CASES)])
+def test_fuzz_append(i):
+    """pa_decode_append against the three separate calls (bit for bit) and
+    the oracle."""
+    wl = _workload("append", i)
+    err = _append_case(wl)
+    log(f"[fuzz append {i}] max abs err {err:.3e}")
+    assert err <= TOL[workloads.BF16]
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"append8-{i}" for i in range(N_CASES)])
+def test_fuzz_fp8_append(i):
+    wl = _workload("append8", i, fp8=True)
+    err = _fp8_append_case(wl)
+    log(f"[fuzz fp8 append {i}] max abs err {err:.3e}")
+    assert err <= TOL8

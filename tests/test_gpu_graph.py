@@ -167,3 +167,37 @@ def test_graph_decode_shared_prefix():
                                      wl.max_seq_len, wl.scale, pb, block_refcounts=rc,
                                      out=out, workspace=ws)
     _replays_match(step, out, "pa_reshape_and_cache + pa_decode_shared_prefix")
+
+
+def test_graph_decode_append():
+    """The appending decode (slot computation, cache write and attention in
+    one call) captured and replayed: every replay writes the same new tokens
+    and reproduces the eager output and pools."""
+    wl = _decode_batch()
+    t = wl.tensors
+    B, D, S, Hq = 16, 128, wl.num_seqs, 32
+    bt, lens = wl.block_tables_tensor("cuda"), wl.seq_lens_tensor("cuda")
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(binding.decode_workspace_bytes(S, Hq, D, wl.max_seq_len, B),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.decode_append(t["query"], t["key"], t["value"], t["k_cache"], t["v_cache"], bt,
+                              lens, wl.max_seq_len, wl.scale, out=out, workspace=ws)
+    _replays_match(step, out, "pa_decode_append")
+
+
+def test_graph_decode_fp8_append():
+    wl = _decode_batch(fp8=True)
+    t = wl.tensors
+    B, D, S, Hq = 16, 128, wl.num_seqs, 32
+    bt, lens = wl.block_tables_tensor("cuda"), wl.seq_lens_tensor("cuda")
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(binding.decode_fp8_workspace_bytes(S, Hq, D, wl.max_seq_len, B),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.decode_fp8_append(t["query"], t["key"], t["value"], t["k_cache8"],
+                                  t["v_cache8"], t["k_scales"], t["v_scales"], bt, lens,
+                                  wl.max_seq_len, wl.scale, out=out, workspace=ws)
+    _replays_match(step, out, "pa_decode_fp8_append")
