@@ -206,9 +206,10 @@ int pa_decode(void* out, const void* query, const void* k_cache,
  * outside [0, num_blocks) (a negative or out-of-range slot in
  * pa_reshape_and_cache).  The attention then includes that token.  On the
  * balanced decode (bf16, block_size >= 8, kv_split_tokens 0, up to 4096
- * sequences) the writes happen inside the attention launch: the wave that
- * reads a sequence's last key step writes its new token first.  Other
- * shapes write them in a launch of their own before the attention.
+ * sequences) everything happens in the attention launch: the wave that
+ * reads a sequence's last key step takes the new token's K/V from key /
+ * value and writes its slot once its work is done.  Other shapes write the
+ * new tokens in a launch of their own before the attention.
  * Workspace as for pa_decode (pa_decode_workspace_bytes).  Two sequences
  * whose new tokens share a slot are undefined (PA_ERR_INDEX under
  * PA_CHECK); key or value NULL with num_seqs > 0 is PA_ERR_NULL.

@@ -46,8 +46,8 @@ struct AttnArgs {
   int32_t prefix_slots;
   // Appending decode (pa_decode_append, pa_decode_fp8_append): the new
   // token of every sequence, key and value rows [num_seqs, Hkv, D] (the
-  // pool dtype; bf16 for an e4m3 pool), written at position seq_len - 1
-  // before the attention reads it.  nullptr: nothing is written.
+  // pool dtype; bf16 for an e4m3 pool), attended to and written at
+  // position seq_len - 1.  nullptr: nothing is written.
   const void* new_k;
   const void* new_v;
 };

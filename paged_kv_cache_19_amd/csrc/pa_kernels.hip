@@ -1143,11 +1143,12 @@ __device__ __forceinline__ void decode_prefix_scan(int* P, int S, int lane) {
 // PREFIX: the shared-prefix work list (prefix items after the sequences'
 // own items); an instantiation without it holds no prefix path, so the
 // plain decode keeps its register budget.
-// APPEND: the appending decode.  The wave whose piece holds an item's last
-// step writes the sequence's new token for that KV head before it loads
-// anything of the piece: that step is the only one that reads the slot, so
-// no other wave waits for the write.  A separate instantiation, so that the
-// plain decode's K/V stay read-only to the compiler.
+// APPEND: the appending decode.  Only an item's last step reads the slot of
+// the sequence's new token; the wave whose piece holds that step takes the
+// token's K/V from the call's rows (NewToken / NewToken8 patches of the
+// step's fragments) and writes the slot after its whole share, so no load
+// waits for a store.  A separate instantiation, so that the plain decode's
+// K/V stay read-only to the compiler.
 template <int D, bool FP8, int NSETS, bool PREFIX = false, bool APPEND = false>
 __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, const int* Ls,
                                              int64_t N, int64_t weff, int w,
