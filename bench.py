@@ -7,8 +7,9 @@ attention.  For the decode workloads that is one pa_decode_append call
 (pa_decode_fp8_append on the e4m3 cache), which computes each sequence's
 new slot, writes its K/V and attends in one launch, then merges; with
 ``--no-append``, and always for the prefill + decode mix (pa_chunked_prefill)
-and the shared-prefix decode, the three calls pa_compute_slot_mapping,
-pa_reshape_and_cache and the attention call.  The separate calls are timed
+the three calls pa_compute_slot_mapping, pa_reshape_and_cache and the
+attention call (the shared-prefix decode has its own appending call,
+pa_decode_shared_prefix_append).  The separate calls are timed
 in every run (``cache_write``, and ``separate_calls`` beside an appending
 step).  Inputs are resident in HBM before the timed region.
 
@@ -235,10 +236,11 @@ def parse():
                         "heads of the workload (tp divides H_kv)")
     p.add_argument("--append", action=argparse.BooleanOptionalAction, default=True,
                    help="decode workloads: the step is one pa_decode_append (or "
-                        "pa_decode_fp8_append) call, which computes the new tokens' slots, "
-                        "writes them and attends in one launch plus the merge (default); "
-                        "--no-append times the three separate calls instead.  The separate "
-                        "calls are timed either way")
+                        "pa_decode_fp8_append, or with --shared-prefix "
+                        "pa_decode_shared_prefix_append) call, which computes the new tokens' "
+                        "slots, writes them and attends in one launch plus the merge "
+                        "(default); --no-append times the three separate calls instead.  The "
+                        "separate calls are timed either way")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="also run one plain device copy of BYTES bytes (a reference for "
                         "hardware byte counters)")
@@ -433,10 +435,17 @@ def main():
                            wl.scale, kv_split_tokens=args.kv_split, block_refcounts=refcounts,
                            out=out, workspace=ws)
 
-    append = args.append and not chunked and not args.shared_prefix
+    append = args.append and not chunked
 
     def attention_append():
-        if fp8:
+        if args.shared_prefix:
+            kc, vc = (t["k_cache8"], t["v_cache8"]) if fp8 else (t["k_cache"], t["v_cache"])
+            scales = dict(k_scales=t["k_scales"], v_scales=t["v_scales"]) if fp8 else {}
+            binding.decode_shared_prefix_append(t["query"], t["key"], t["value"], kc, vc, bt, lens,
+                                                wl.max_seq_len, wl.scale, prefix_blocks,
+                                                block_refcounts=refcounts, out=out, workspace=ws,
+                                                **scales)
+        elif fp8:
             binding.decode_fp8_append(t["query"], t["key"], t["value"], t["k_cache8"],
                                       t["v_cache8"], t["k_scales"], t["v_scales"], bt, lens,
                                       wl.max_seq_len, wl.scale, block_refcounts=refcounts,
@@ -531,8 +540,11 @@ def main():
         "pa_decode_fp8" if fp8 else "pa_decode")
     if args.shared_prefix:
         call = "pa_decode_shared_prefix"
+    separate_call = call
     if append:  # the roofline covers the appending call, which is the whole step
         call = "pa_decode_fp8_append" if fp8 else "pa_decode_append"
+        if args.shared_prefix:
+            call = "pa_decode_shared_prefix_append"
         attn_ms = fused_ms
     attn_avg = sum(attn_ms) / len(attn_ms)
     print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, {call} avg "
@@ -657,8 +669,7 @@ def main():
     }
     if append:
         result["separate_calls"] = {
-            "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + "
-                    f"{'pa_decode_fp8' if fp8 else 'pa_decode'}",
+            "step": f"slot mapping + reshape_and_cache{'_fp8' if fp8 else ''} + {separate_call}",
             "ms_per_step": round(separate_ms, 5),
             "attention_avg_ms": round(sum(sep_attn_ms) / len(sep_attn_ms), 5),
         }

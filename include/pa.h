@@ -80,8 +80,9 @@
  *    this header needs no HIP header.
  *  - Added entry points: pa_compute_slot_mapping (the slot step on the
  *    device), pa_version, the e4m3 cache calls, pa_decode_shared_prefix,
- *    the whole-block copies, and pa_decode_append / pa_decode_fp8_append
- *    (slot computation, cache write and decode of one step in one call).
+ *    the whole-block copies, and pa_decode_append / pa_decode_fp8_append /
+ *    pa_decode_shared_prefix_append (slot computation, cache write and
+ *    decode of one step in one call).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -477,6 +478,36 @@ int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, int32_t prefix_blocks, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_shared_prefix_append -- pa_decode_shared_prefix with the step's
+ * slot computation and cache write in the same call, as pa_decode_append
+ * adds them to pa_decode (passages cited there): key, value [num_seqs,
+ * num_kv_heads, head_dim] (bf16) are each sequence's new token, written at
+ * position seq_lens[s] - 1 (quantised as pa_reshape_and_cache_fp8 does when
+ * the scales are given) and attended to.  The same results, bit for bit, as
+ * pa_compute_slot_mapping + pa_reshape_and_cache[_fp8] +
+ * pa_decode_shared_prefix.  Every sequence must hold more than the prefix
+ * (seq_lens[s] > prefix_blocks * block_size), so that no new token lands in
+ * a shared block (PA_ERR_INDEX under PA_CHECK; undefined otherwise).
+ * Workspace: pa_decode_shared_prefix_workspace_bytes.  Arguments and limits
+ * otherwise as for pa_decode_shared_prefix.
+ */
+int pa_decode_shared_prefix_append(void* out, const void* query,
+                                   const void* key, const void* value,
+                                   void* k_cache, void* v_cache,
+                                   const float* k_scales,
+                                   const float* v_scales,
+                                   const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq,
+                                   const int32_t* block_refcounts,
+                                   const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t max_seq_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks,
+                                   int32_t prefix_blocks, float scale,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* ------------------------------------------------------------------------
  * For callers that cannot allocate device memory (code under stream

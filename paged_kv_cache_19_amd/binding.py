@@ -72,6 +72,10 @@ SIGNATURES = {
     "pa_decode_fp8_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                             _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _f32, _vp, _sz, _vp]),
+    "pa_decode_shared_prefix_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                      _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                      _i32, _i32, _i32, _i32, _f32, _vp, _sz,
+                                                      _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -620,6 +624,49 @@ def decode_shared_prefix(query: torch.Tensor, k_cache: torch.Tensor, v_cache: to
         _ptr(block_tables), block_tables.shape[1], _ptr(block_refcounts), _ptr(seq_lens), S,
         max_seq_len, Hq, Hkv, D, B, NB, prefix_blocks, scale, _ptr(workspace),
         workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_shared_prefix_append(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                max_seq_len: int, scale: float, prefix_blocks: int,
+                                k_scales: Optional[torch.Tensor] = None,
+                                v_scales: Optional[torch.Tensor] = None,
+                                block_refcounts: Optional[torch.Tensor] = None,
+                                out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """pa_decode_shared_prefix_append: each sequence's new token (bf16
+    key/value [S, H_kv, D]) written at position seq_len - 1 (quantised for
+    e4m3 pools) and the shared-prefix decode, in one call."""
+    if query.dtype != torch.bfloat16:
+        raise ValueError("the shared-prefix decode takes a bf16 query")
+    if (k_scales is None) != (v_scales is None):
+        raise ValueError("pass both k_scales and v_scales (e4m3 pools) or neither")
+    if k_scales is not None:
+        NB, Hkv, B, D = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    else:
+        NB, Hkv, B, D = _pools(k_cache, v_cache)
+        _want(k_cache.dtype == torch.bfloat16, "without scales the pools are bf16")
+    _rows(query, out, Hkv, D)
+    S, Hq = query.shape[0], query.shape[1]
+    _new_tokens(key, value, S, Hkv, D, torch.bfloat16)
+    _metadata(block_tables, seq_lens, S, block_refcounts, NB)
+    _workspace(workspace)
+    _same_device(query, key, value, k_cache, v_cache, k_scales, v_scales, block_tables,
+                 seq_lens, block_refcounts, out, workspace)
+    if out is None:
+        out = torch.empty_like(query)
+    if workspace is None:  # needs no initialisation
+        workspace = torch.empty(decode_shared_prefix_workspace_bytes(S, Hq, D, max_seq_len, B,
+                                                                     prefix_blocks),
+                                dtype=torch.uint8, device=query.device)
+    _check("pa_decode_shared_prefix_append", lib().pa_decode_shared_prefix_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), block_tables.shape[1],
+        _ptr(block_refcounts), _ptr(seq_lens), S, max_seq_len, Hq, Hkv, D, B, NB, prefix_blocks,
+        scale, _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -202,9 +202,11 @@ int validate_scales(const float* d_ks, const float* d_vs, int num_blocks, int nu
 }
 
 // PA_CHECK for a shared prefix: every table starts with row 0's first
-// prefix_blocks entries and every sequence holds at least the prefix.
+// prefix_blocks entries and every sequence holds at least the prefix (past
+// it with `past`: an appending call's new token must not land in a shared
+// block).
 int validate_prefix(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, int num_seqs,
-                    int prefix_blocks, int block_size, hipStream_t st) {
+                    int prefix_blocks, int block_size, hipStream_t st, bool past = false) {
   if (prefix_blocks > max_blocks) return PA_ERR_INDEX;
   std::vector<int32_t> bt((size_t)num_seqs * max_blocks), lens(num_seqs);
   if (hipMemcpyAsync(bt.data(), d_bt, bt.size() * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
@@ -213,7 +215,7 @@ int validate_prefix(const int32_t* d_bt, int max_blocks, const int32_t* d_lens, 
       hipStreamSynchronize(st) != hipSuccess)
     return PA_ERR_HIP;
   for (int s = 0; s < num_seqs; ++s) {
-    if ((int64_t)lens[s] < (int64_t)prefix_blocks * block_size) return PA_ERR_INDEX;
+    if ((int64_t)lens[s] < (int64_t)prefix_blocks * block_size + (past ? 1 : 0)) return PA_ERR_INDEX;
     for (int b = 0; b < prefix_blocks; ++b)
       if (bt[(size_t)s * max_blocks + b] != bt[b]) return PA_ERR_INDEX;
   }
@@ -321,7 +323,7 @@ int attention_common(void* out, const void* query, const void* k_cache, const vo
     if (rc != PA_OK) return rc;
     if (prefix_blocks > 0) {
       rc = validate_prefix(block_tables, max_blocks, seq_lens, num_seqs, prefix_blocks,
-                           block_size, st);
+                           block_size, st, new_k != nullptr);
       if (rc != PA_OK) return rc;
     }
     if (new_k) {
@@ -435,6 +437,43 @@ int validate_stage_capacity(const int32_t* d_lens, const int32_t* d_qsl, int num
     if (qsl[s + 1] - qsl[s] > 1)
       need += std::min((std::max(lens[s], 0) + block_size - 1) / block_size, max_blocks);
   return need <= cap ? PA_OK : PA_ERR_INDEX;
+}
+
+// pa_decode_shared_prefix, with (append) or without the new tokens' write.
+int shared_prefix_common(void* out, const void* query, const void* key, const void* value,
+                         const void* k_cache, const void* v_cache, const float* k_scales,
+                         const float* v_scales, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* block_refcounts,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t prefix_blocks,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream,
+                         bool append) {
+  if (prefix_blocks < 0 || (k_scales == nullptr) != (v_scales == nullptr)) return PA_ERR_SHAPE;
+  const bool fp8 = k_scales != nullptr;
+  if (block_size > 0 && block_size < (fp8 ? 16 : 8)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)prefix_blocks * block_size > max_seq_len ||
+      prefix_blocks > max_blocks_per_seq)
+    return PA_ERR_SHAPE;
+  // Without a whole prefix step there is no prefix entry: pa_decode's (or
+  // pa_decode_fp8's) limits apply, including the bf16 fixed-split fallback.
+  const int pstep = fp8 ? 64 : 32;
+  const int64_t prefix_keys = block_size > 0 ? (int64_t)prefix_blocks * block_size / pstep * pstep : 0;
+  if (prefix_keys > 0 && num_q_heads > 0 && num_kv_heads > 0 &&
+      num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 16) {
+    const int spg = 16 * pa::prefix_tiles(fp8) / (num_q_heads / num_kv_heads);
+    if ((int64_t)num_seqs + (num_seqs + spg - 1) / spg > kMaxBalancedSeqs)
+      return PA_ERR_UNSUPPORTED;
+  }
+  Fp8Kv f8;
+  f8.kv_fp8 = fp8 ? 1 : 0;
+  f8.k_scales = k_scales;
+  f8.v_scales = v_scales;
+  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                          PA_BF16, 0, workspace, workspace_bytes, stream, f8, prefix_blocks,
+                          append, key, value);
 }
 
 }  // namespace
@@ -726,30 +765,27 @@ int pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, int32_t prefix_blocks, float scale,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  if (prefix_blocks < 0 || (k_scales == nullptr) != (v_scales == nullptr)) return PA_ERR_SHAPE;
-  const bool fp8 = k_scales != nullptr;
-  if (block_size > 0 && block_size < (fp8 ? 16 : 8)) return PA_ERR_UNSUPPORTED;
-  if ((int64_t)prefix_blocks * block_size > max_seq_len ||
-      prefix_blocks > max_blocks_per_seq)
-    return PA_ERR_SHAPE;
-  // Without a whole prefix step there is no prefix entry: pa_decode's (or
-  // pa_decode_fp8's) limits apply, including the bf16 fixed-split fallback.
-  const int pstep = fp8 ? 64 : 32;
-  const int64_t prefix_keys = block_size > 0 ? (int64_t)prefix_blocks * block_size / pstep * pstep : 0;
-  if (prefix_keys > 0 && num_q_heads > 0 && num_kv_heads > 0 &&
-      num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 16) {
-    const int spg = 16 * pa::prefix_tiles(fp8) / (num_q_heads / num_kv_heads);
-    if ((int64_t)num_seqs + (num_seqs + spg - 1) / spg > kMaxBalancedSeqs)
-      return PA_ERR_UNSUPPORTED;
-  }
-  Fp8Kv f8;
-  f8.kv_fp8 = fp8 ? 1 : 0;
-  f8.k_scales = k_scales;
-  f8.v_scales = v_scales;
-  return attention_common(out, query, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                          block_refcounts, seq_lens, nullptr, num_seqs, num_seqs, max_seq_len, 1,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                          PA_BF16, 0, workspace, workspace_bytes, stream, f8, prefix_blocks);
+  return shared_prefix_common(out, query, nullptr, nullptr, k_cache, v_cache, k_scales, v_scales,
+                              block_tables, max_blocks_per_seq, block_refcounts, seq_lens,
+                              num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                              block_size, num_blocks, prefix_blocks, scale, workspace,
+                              workspace_bytes, stream, false);
+}
+
+int pa_decode_shared_prefix_append(void* out, const void* query, const void* key,
+                                   const void* value, void* k_cache, void* v_cache,
+                                   const float* k_scales, const float* v_scales,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* block_refcounts, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, int32_t prefix_blocks, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return shared_prefix_common(out, query, key, value, k_cache, v_cache, k_scales, v_scales,
+                              block_tables, max_blocks_per_seq, block_refcounts, seq_lens,
+                              num_seqs, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                              block_size, num_blocks, prefix_blocks, scale, workspace,
+                              workspace_bytes, stream, true);
 }
 
 int pa_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,

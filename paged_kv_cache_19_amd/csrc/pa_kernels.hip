@@ -417,6 +417,16 @@ struct NewToken {
   uint32_t v[D / 16]; // the lane's V entries, in place within dword vd
 };
 
+// The same token with its K row and V column (D bf16 each, head_dim order)
+// in LDS instead, for kernels whose registers are full (the shared-prefix
+// decode).
+struct NewTokenL {
+  int c;                // as NewToken
+  bool ka, kb, v_sel;   // this lane's K fragments / a V element hold it
+  int vd, sh;           // dword and bit offset of its V element
+  const uint16_t* row;  // LDS: K row [D], then V column [D]
+};
+
 // Rescaling of the running output is skipped while a chunk's maximum stays
 // within this many powers of two of the running maximum: the exponentials
 // are then at most 2^8 and the final o / l is unchanged.
@@ -534,10 +544,12 @@ __device__ __forceinline__ int leading_shared_keys(const AttnArgs& a, const SeqV
 // Cache policy: with STREAM every K/V load is non-temporal (private blocks
 // are read once per call); without it loads go through the caches (shared
 // prefix blocks, and query chunks whose K/V several waves re-read).
-template <int D, int R, bool STREAM, int NSETS = 2, bool PATCH = false>
+// PATCH: 0 none, 1 the new token from registers (nt), 2 from LDS (ntl).
+template <int D, int R, bool STREAM, int NSETS = 2, int PATCH = 0>
 __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int kv_wave, int kv_min,
                                        int k_begin, int k_end, RowState<D, R>& st,
-                                       const NewToken<D>* nt = nullptr) {
+                                       const NewToken<D>* nt = nullptr,
+                                       const NewTokenL* ntl = nullptr) {
   constexpr int KK = D / 32;
   constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -585,7 +597,28 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const SeqView& v, int 
 
   auto compute = [&](KVFrag<D>& f, int c) {
     const int pv_ = c + 8 * j4;
-    if constexpr (PATCH) {
+    if constexpr (PATCH == 2) {
+      // as below, from LDS
+      if (c == ntl->c) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(ntl->row + 8 * j4 + 32 * kk);
+          f.ka[kk] = ntl->ka ? x : f.ka[kk];
+          f.kb[kk] = ntl->kb ? x : f.kb[kk];
+        }
+        const uint32_t vmask = ntl->v_sel ? 0xFFFFu << ntl->sh : 0u;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint32_t val = (uint32_t)ntl->row[D + i + 16 * n] << ntl->sh;
+          u32x4 x = __builtin_bit_cast(u32x4, f.v[n]);
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            x[d] = d == ntl->vd ? ((x[d] & ~vmask) | (val & vmask)) : x[d];
+          f.v[n] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+    }
+    if constexpr (PATCH == 1) {
       // the step holding an appending call's new token: its K/V come from
       // the call's key / value rows, not from the slot (written later)
       if (c == nt->c) {
@@ -1261,7 +1294,35 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
         }
       }
     }
-    if constexpr (APPEND && !FP8) {
+    NewTokenL ntl;
+    ntl.c = -1;
+    if constexpr (APPEND && !FP8 && PREFIX) {
+      if (new_id >= 0 && new_id < a.num_blocks) {  // exactly when the write happens
+        const int lane = threadIdx.x & 63;
+        const int u = new_pos & 31;
+        const bool b = (u & 4) != 0;
+        const int ua = b ? u - 4 : u;
+        const bool krow = (lane & 15) == 4 * (ua >> 3) + (ua & 3);
+        ntl.c = new_pos - u;
+        ntl.ka = krow && !b;
+        ntl.kb = krow && b;
+        ntl.v_sel = (lane >> 4) == (u >> 3);
+        ntl.vd = (u & 7) >> 1;
+        ntl.sh = 16 * (u & 1);
+        uint16_t* row = reinterpret_cast<uint16_t*>(tok_lds);
+        ntl.row = row;
+        constexpr int PER = D / 64;
+        const int64_t src = ((int64_t)r0 * Hkv + kvh) * D + PER * lane;
+        const uint16_t* nk = static_cast<const uint16_t*>(a.new_k) + src;
+        const uint16_t* nv = static_cast<const uint16_t*>(a.new_v) + src;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          row[PER * lane + e] = nk[e];
+          row[D + PER * lane + e] = nv[e];
+        }
+      }
+    }
+    if constexpr (APPEND && !FP8 && !PREFIX) {
       const int pos = new_pos;
       const int id = new_id;
       if (id >= 0 && id < a.num_blocks) {  // exactly when the write happens
@@ -1289,7 +1350,7 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
           nt.v[n] = vcol ? (uint32_t)nv[(lane & 15) + 16 * n] << sh : 0u;
       }
     }
-    constexpr bool PATCH = APPEND && !FP8;
+    constexpr int PATCH = APPEND && !FP8 ? (PREFIX ? 2 : 1) : 0;
     RowState<D, 1> st;
     load_rows<D, 1, FP8>(a, v, 0, st);
     const int kb0 = a.prefix_keys;  // step 0 of an own item starts after the shared prefix
@@ -1309,9 +1370,9 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
         attend_fp8<D, true, 1, NSETS, PATCH8>(a, v, kl, kl, max(k_begin, k_sh), k_end, st, &nt8);
     } else {
       if (k_sh > k_begin)
-        attend<D, 1, false, NSETS, PATCH>(a, v, kl, kl, k_begin, min(k_sh, k_end), st, &nt);
+        attend<D, 1, false, NSETS, PATCH>(a, v, kl, kl, k_begin, min(k_sh, k_end), st, &nt, &ntl);
       if (k_end > max(k_begin, k_sh))
-        attend<D, 1, true, NSETS, PATCH>(a, v, kl, kl, max(k_begin, k_sh), k_end, st, &nt);
+        attend<D, 1, true, NSETS, PATCH>(a, v, kl, kl, max(k_begin, k_sh), k_end, st, &nt, &ntl);
     }
     if (a.prefix_keys > 0) {
       // every row is merged with its prefix part: own pieces in slots
@@ -1341,7 +1402,7 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
       const int c0 = (int)max((int64_t)0, g2 - g_item);
       const int c1 = (int)min((int64_t)nch, g_end - g_item);
       g2 = g_item + nch;
-      if (c1 <= c0 || c1 != nch) continue;
+      if (c1 <= c0 || c1 != nch || (PREFIX && s2 >= a.num_seqs)) continue;  // prefix items hold none
       int r0, qn;
       seq_rows(a.query_start_loc, s2, a.num_tokens, r0, qn);
       append_token<2, D, FP8, false>(a, s2, kvh, Ls[s2], r0);
@@ -2446,22 +2507,25 @@ hipError_t resident(Residency& c, K kernel, int threads, size_t lds, int seqs, i
 
 template <int D, bool FP8 = false>
 hipError_t launch_streamk(const AttnArgs& a, void* header, hipStream_t st) {
-  static thread_local Residency cache, cache_p, cache_a;
+  static thread_local Residency cache, cache_p, cache_a, cache_pa;
   const int entries = a.num_seqs + prefix_items(a.num_seqs, a.prefix_group);
   const bool prefix = a.prefix_keys > 0;
-  const bool append = a.new_k != nullptr;  // never together with a prefix (host)
-  // P and Ls, then (appending e4m3 decode) the new token's 2 * D codes at a
-  // 16-byte boundary
-  const size_t lds = append && FP8 ? (size_t)((2 * entries + 1 + 3) & ~3) * sizeof(int) + 2 * D
-                                   : (size_t)(2 * entries + 1) * sizeof(int);
+  const bool append = a.new_k != nullptr;
+  // P and Ls, then (appending decode) the new token's K row and V column at a
+  // 16-byte boundary: 2 * D e4m3 codes, or 2 * D bf16 values
+  const size_t lds = append ? (size_t)((2 * entries + 1 + 3) & ~3) * sizeof(int) + (FP8 ? 2 : 4) * D
+                            : (size_t)(2 * entries + 1) * sizeof(int);
   int waves = 0;
   hipError_t err =
-      prefix ? resident(cache_p, decode_streamk_kernel<D, FP8, true>, 64, lds, entries, waves)
+      prefix && append
+          ? resident(cache_pa, decode_streamk_kernel<D, FP8, true, true>, 64, lds, entries, waves)
+      : prefix ? resident(cache_p, decode_streamk_kernel<D, FP8, true>, 64, lds, entries, waves)
       : append ? resident(cache_a, decode_streamk_kernel<D, FP8, false, true>, 64, lds, entries, waves)
                : resident(cache, decode_streamk_kernel<D, FP8>, 64, lds, entries, waves);
   if (err != hipSuccess) return err;
   StreamKHeader* hdr = static_cast<StreamKHeader*>(header);
-  if (prefix) decode_streamk_kernel<D, FP8, true><<<waves, 64, lds, st>>>(a, waves, hdr);
+  if (prefix && append) decode_streamk_kernel<D, FP8, true, true><<<waves, 64, lds, st>>>(a, waves, hdr);
+  else if (prefix) decode_streamk_kernel<D, FP8, true><<<waves, 64, lds, st>>>(a, waves, hdr);
   else if (append) decode_streamk_kernel<D, FP8, false, true><<<waves, 64, lds, st>>>(a, waves, hdr);
   else decode_streamk_kernel<D, FP8><<<waves, 64, lds, st>>>(a, waves, hdr);
   err = hipGetLastError();

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(binding.SIGNATURES)
@@ -179,6 +179,27 @@ def test_appending_decode_rejects_bad_arguments(lib, fp8, kw, code):
     assert _append(lib, fp8=fp8, **kw) == code
 
 
+def _shared_append(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None, bt=FAKE,
+             maxb=4, lens=FAKE, S=2, maxlen=64, Hq=8, Hkv=2, D=128, B=16, NB=8, pb=2, scale=0.1,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode_shared_prefix_append(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"],
+                                              a["ks"], a["vs"], a["bt"], a["maxb"], None,
+                                              a["lens"], a["S"], a["maxlen"], a["Hq"], a["Hkv"],
+                                              a["D"], a["B"], a["NB"], a["pb"], a["scale"],
+                                              a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1), (dict(pb=-1), -2),
+    (dict(ks=FAKE), -2), (dict(ks=FAKE, vs=FAKE, B=8), -4), (dict(pb=5), -2), (dict(D=96), -4),
+    (dict(ws=None), -5), (dict(wsb=16), -5), (dict(S=4000), -4),
+])
+def test_shared_prefix_append_rejects_bad_arguments(lib, kw, code):
+    assert _shared_append(lib, **kw) == code
+
+
 def test_appending_decode_limits_and_empty_batch(lib):
     assert _append(lib, S=0, k=None, v=None, out=None) == 0
     assert _append(lib, fp8=True, S=0, k=None, v=None, out=None) == 0
@@ -187,6 +208,7 @@ def test_appending_decode_limits_and_empty_batch(lib):
     assert _append(lib, fp8=True, S=5000) == -4    # the e4m3 decode stops at 4,096
     assert _append(lib, dtype=7) == -3
     assert _append(lib, split=96) == -2
+    assert _shared_append(lib, S=0, k=None, v=None, out=None) == 0
 
 
 def _shared(lib, **kw):

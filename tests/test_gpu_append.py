@@ -194,3 +194,90 @@ def test_fp8_append_matches_separate_calls_and_oracle(name):
     err = _fp8_append_case(wl)
     log(f"[append fp8] {name}: max abs err vs oracle {err:.3e}")
     assert err <= TOL[workloads.BF16]
+
+
+def _shared_append_case(wl, prefix_blocks, fp8=False):
+    """pa_decode_shared_prefix_append against the three separate calls (pools
+    and output bit for bit) and the oracle."""
+    t = wl.tensors
+    dev = wl.device
+    B = wl.shape.block_size
+    if fp8:
+        _poison_fp8(wl)
+        kc, vc = t["k_cache8"], t["v_cache8"]
+        sc = dict(k_scales=t["k_scales"], v_scales=t["v_scales"])
+    else:
+        poison(wl)
+        kc, vc = t["k_cache"], t["v_cache"]
+        sc = {}
+    bt = wl.block_tables_tensor(dev)
+    lens = wl.seq_lens_tensor(dev)
+    rc = wl.block_refcounts_tensor(dev)
+    kc0, vc0 = kc.clone(), vc.clone()
+    slots = binding.compute_slot_mapping(bt, lens, None, B)
+    if fp8:
+        binding.reshape_and_cache_fp8(t["key"], t["value"], kc, vc, sc["k_scales"],
+                                      sc["v_scales"], slots)
+    else:
+        binding.reshape_and_cache(t["key"], t["value"], kc, vc, slots)
+    want = binding.decode_shared_prefix(t["query"], kc, vc, bt, lens, wl.max_seq_len, wl.scale,
+                                        prefix_blocks, block_refcounts=rc, **sc)
+    kc1, vc1 = kc0.clone(), vc0.clone()
+    got = binding.decode_shared_prefix_append(t["query"], t["key"], t["value"], kc1, vc1, bt, lens,
+                                              wl.max_seq_len, wl.scale, prefix_blocks,
+                                              block_refcounts=rc, **sc)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(kc1.cpu()) if not fp8 else kc1.cpu(),
+                       bits(kc.cpu()) if not fp8 else kc.cpu()), "K pools differ"
+    assert torch.equal(bits(vc1.cpu()) if not fp8 else vc1.cpu(),
+                       bits(vc.cpu()) if not fp8 else vc.cpu()), "V pools differ"
+    got_c = got.cpu()
+    assert torch.isfinite(got_c.float()).all(), "non-finite output (a poisoned slot was read)"
+    assert torch.equal(bits(got_c), bits(want.cpu())), "output differs from the separate calls"
+    slots_ref = ref.compute_slot_mapping(bt.cpu(), wl.seq_lens, None, B)
+    if fp8:
+        ks, vs = sc["k_scales"].cpu(), sc["v_scales"].cpu()
+        kq, vq = ref8.reshape_and_cache_fp8(kc0.cpu(), vc0.cpu(), ks, vs, t["key"].cpu(),
+                                            t["value"].cpu(), slots_ref)
+        assert torch.equal(kc1.cpu(), kq) and torch.equal(vc1.cpu(), vq), "pools differ from the oracle"
+        expect = ref8.decode_fp8(t["query"].cpu(), kq, vq, ks, vs, bt.cpu(), wl.seq_lens, wl.scale)
+    else:
+        kr, vr = ref.reshape_and_cache(kc0.cpu(), vc0.cpu(), t["key"].cpu(), t["value"].cpu(),
+                                       slots_ref)
+        assert torch.equal(bits(kc1.cpu()), bits(kr)) and torch.equal(bits(vc1.cpu()), bits(vr)), \
+            "pools differ from the oracle"
+        expect = ref.decode(t["query"].cpu(), kr, vr, bt.cpu(), wl.seq_lens, wl.scale)
+    return (got_c.double() - expect).abs().max().item()
+
+
+SHARED_CASES = {
+    # name: (Hq, Hkv, D, B, prefix tokens, seq_lens or None for workload 4)
+    "workload4": None,
+    "g1-b16": (8, 8, 128, 16, 512, [513, 600, 1500, 520, 777]),
+    "g16-b32": (32, 2, 128, 32, 256, [257, 290, 1000, 300]),
+    "g4-b8-d64": (16, 4, 64, 8, 128, [129, 130, 500, 137, 1200, 133]),
+    "b64": (32, 8, 128, 64, 640, [641, 700, 2000, 1000]),
+    "prefix-under-a-step": (32, 8, 128, 16, 16, [17, 40, 300, 100]),
+}
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("name", sorted(SHARED_CASES))
+def test_shared_prefix_append_matches_separate_calls_and_oracle(name, fp8):
+    case = SHARED_CASES[name]
+    if case is None:
+        wl = workloads.make_workload(4, device="cuda", kv_fp8=fp8)
+        prefix_blocks = len(wl.shared_blocks)
+    else:
+        Hq, Hkv, D, B, prefix, lens = case
+        if fp8 and B < 16:
+            pytest.skip("e4m3 pools need 16-token blocks or more")
+        wl = workloads.make_workload(2, seed=71, device="cuda", seq_lens=lens,
+                                     shape=_shape("sp-append", Hq, Hkv, D, B),
+                                     shared_prefix_tokens=prefix, kv_fp8=fp8)
+        prefix_blocks = prefix // B
+    log(f"[append shared] {name} {'fp8' if fp8 else 'bf16'}: {wl.num_seqs} sequences, "
+        f"prefix {prefix_blocks} blocks of {wl.shape.block_size}")
+    err = _shared_append_case(wl, prefix_blocks, fp8)
+    log(f"[append shared] {name}: max abs err vs oracle {err:.3e}")
+    assert err <= TOL[workloads.BF16]

@@ -13,7 +13,7 @@ import pytest
 
 from paged_kv_cache_19_amd import workloads
 from tests.gpu_common import TOL, log, run_and_compare
-from tests.test_gpu_append import _append_case, _fp8_append_case
+from tests.test_gpu_append import _append_case, _fp8_append_case, _shared_append_case
 from tests.test_gpu_fp8 import TOL as TOL8
 from tests.test_gpu_fp8 import _run_fp8, _run_fp8_chunked
 from tests.test_gpu_shared_prefix import TOL as TOL_SP
@@ -145,3 +145,19 @@ def test_fuzz_fp8_append(i):
     err = _fp8_append_case(wl)
     log(f"[fuzz fp8 append {i}] max abs err {err:.3e}")
     assert err <= TOL8
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("i", range(N_CASES), ids=[f"shared-append-{i}" for i in range(N_CASES)])
+def test_fuzz_shared_prefix_append(i, fp8):
+    """pa_decode_shared_prefix_append on the shared-prefix draws (every
+    sequence holds at least one position past the prefix)."""
+    Hq, Hkv, D, B, prefix, lens = draw_shared(fp8, i)
+    log(f"[fuzz shared append {'fp8' if fp8 else 'bf16'} {i}] Hq={Hq} Hkv={Hkv} D={D} B={B} "
+        f"prefix={prefix} S={len(lens)} max_len={max(lens)}")
+    shape = workloads.Shape("fuzz-shared-append", workloads.BF16, Hq, Hkv, D, B)
+    wl = workloads.make_workload(2, seed=700 + i, device="cuda", seq_lens=lens, shape=shape,
+                                 shared_prefix_tokens=prefix, kv_fp8=fp8)
+    err = _shared_append_case(wl, prefix // B, fp8)
+    log(f"[fuzz shared append {i}] max abs err {err:.3e}")
+    assert err <= TOL_SP

@@ -201,3 +201,24 @@ def test_graph_decode_fp8_append():
                                   t["v_cache8"], t["k_scales"], t["v_scales"], bt, lens,
                                   wl.max_seq_len, wl.scale, out=out, workspace=ws)
     _replays_match(step, out, "pa_decode_fp8_append")
+
+
+def test_graph_decode_shared_prefix_append():
+    shape = workloads.Shape("graph-sp-append", workloads.BF16, 32, 8, 128, 16)
+    wl = workloads.make_workload(2, seed=34, device="cuda",
+                                 seq_lens=[600, 513, 1400, 777, 530, 900], shape=shape,
+                                 shared_prefix_tokens=512)
+    t = wl.tensors
+    B, D, S, Hq, pb = 16, 128, wl.num_seqs, 32, 512 // 16
+    bt, lens = wl.block_tables_tensor("cuda"), wl.seq_lens_tensor("cuda")
+    rc = wl.block_refcounts_tensor("cuda")
+    out = torch.empty_like(t["query"])
+    ws = torch.empty(binding.decode_shared_prefix_workspace_bytes(S, Hq, D, wl.max_seq_len, B,
+                                                                  pb),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.decode_shared_prefix_append(t["query"], t["key"], t["value"], t["k_cache"],
+                                            t["v_cache"], bt, lens, wl.max_seq_len, wl.scale, pb,
+                                            block_refcounts=rc, out=out, workspace=ws)
+    _replays_match(step, out, "pa_decode_shared_prefix_append")
