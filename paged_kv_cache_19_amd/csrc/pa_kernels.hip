@@ -296,11 +296,11 @@ __global__ __launch_bounds__(2 * D) void reshape_and_cache_fp8_kernel(
 // reshape_and_cache_fp8_kernel (the same division, clamp and RNE
 // conversion, element by element).  Nothing is written where the table
 // cannot address the position or names a block outside the pool, as with a
-// negative or out-of-range slot there.  One wave, D / 64 elements per lane;
-// with WAIT it returns with the wave's stores complete, so whatever the
-// wave loads next sees them.
+// negative or out-of-range slot there.  One wave, D / 64 elements per lane.
+// Nothing waits for the stores: the attention of the same call takes the
+// token from its rows, and later calls are ordered by the stream.
 // ---------------------------------------------------------------------------
-template <int ES, int D, bool FP8, bool WAIT>
+template <int ES, int D, bool FP8>
 __device__ __forceinline__ void append_token(const AttnArgs& a, int s, int kvh, int L, int t) {
   constexpr int PER = D / 64;  // elements per lane
   static_assert(PER == 1 || PER == 2, "head_dim 64 or 128");
@@ -346,7 +346,6 @@ __device__ __forceinline__ void append_token(const AttnArgs& a, int s, int kvh, 
       vc[vdst + (int64_t)e * B] = nv[e];
     }
   }
-  if constexpr (WAIT) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stores count in vmcnt here
 }
 
 // The appending decode's writes on their own, before an attention path that
@@ -355,7 +354,7 @@ __device__ __forceinline__ void append_token(const AttnArgs& a, int s, int kvh, 
 template <int ES, int D, bool FP8>
 __global__ __launch_bounds__(64) void append_tokens_kernel(AttnArgs a) {
   const int s = blockIdx.x, kvh = blockIdx.y;
-  append_token<ES, D, FP8, false>(a, s, kvh, a.seq_lens[s], s);
+  append_token<ES, D, FP8>(a, s, kvh, a.seq_lens[s], s);
 }
 
 // ---------------------------------------------------------------------------
@@ -851,7 +850,7 @@ __device__ __forceinline__ void attend_fp8(const AttnArgs& a, const SeqView& v, 
     const int pv = c + 16 * j4;
     if constexpr (PATCH) {
       // the step holding an appending call's new token: its codes come from
-      // registers, not from the slot (written after the share)
+      // LDS, not from the slot (written after the share)
       if (c == nt->c) {
         u32x4 kc[KP];
 #pragma unroll
@@ -1250,7 +1249,9 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
     const SeqView v = seq_view(a, s, kvh, Ls[s], r0, 1);
     const int kl = min(v.L, v.kcap);
     // Appending: the step that holds the new token takes its K/V from the
-    // call's rows in registers; the cache write comes after the share (below).
+    // call's rows (bf16: in registers, or in LDS in the shared-prefix
+    // kernel; e4m3: its codes in LDS); the cache write comes after the share
+    // (below).
     NewToken<D> nt;
     NewToken8 nt8;
     nt.c = -1;
@@ -1405,7 +1406,7 @@ __device__ __forceinline__ void decode_share(const AttnArgs& a, const int* P, co
       if (c1 <= c0 || c1 != nch || (PREFIX && s2 >= a.num_seqs)) continue;  // prefix items hold none
       int r0, qn;
       seq_rows(a.query_start_loc, s2, a.num_tokens, r0, qn);
-      append_token<2, D, FP8, false>(a, s2, kvh, Ls[s2], r0);
+      append_token<2, D, FP8>(a, s2, kvh, Ls[s2], r0);
     }
   }
 }
@@ -2015,7 +2016,7 @@ __device__ __forceinline__ void prefill_ranges(const AttnArgs& a, const int* seq
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float p = fast_exp2(fmaf(cur[hf][r], sl2, nm[hf]));
-              t += p;
+              t = r == 0 ? p : t + p;  // p >= +0: the same sum as from 0, one add fewer
               pf[hf][r >> 3][r & 7] = static_cast<__bf16>(p);
             }
             ps[hf] = t;
