@@ -284,3 +284,45 @@ def test_shared_prefix_append_matches_separate_calls_and_oracle(name, fp8):
     err = _shared_append_case(wl, prefix_blocks, fp8)
     log(f"[append shared] {name}: max abs err vs oracle {err:.3e}")
     assert err <= TOL[workloads.BF16]
+
+
+def test_append_pa_check(monkeypatch):
+    """PA_CHECK=1: two sequences whose new tokens would share a slot, and a
+    shared-prefix appending call whose new token would land in a shared
+    block, are refused with PA_ERR_INDEX before anything is launched; the
+    pools stay untouched."""
+    wl = workloads.make_workload(2, seed=95, device="cuda", seq_lens=[40, 33, 17, 64])
+    t = wl.tensors
+    bt = wl.block_tables_tensor("cuda")
+    lens = wl.seq_lens_tensor("cuda")
+    monkeypatch.setenv("PA_CHECK", "1")
+    kc0, vc0 = t["k_cache"].clone(), t["v_cache"].clone()
+    args = (t["query"], t["key"], t["value"], t["k_cache"], t["v_cache"])
+    binding.decode_append(*args, bt, lens, wl.max_seq_len, wl.scale)   # valid
+    torch.cuda.synchronize()
+    # sequence 1 (33 tokens: position 32 = block 2, offset 0) made to write
+    # the slot of sequence 2 (17 tokens: position 16 = block 1, offset 0)
+    bad = bt.clone()
+    bad[1, 2] = bt[2, 1]
+    kc1, vc1 = t["k_cache"].clone(), t["v_cache"].clone()
+    with pytest.raises(binding.PAError) as e:
+        binding.decode_append(*args, bad, lens, wl.max_seq_len, wl.scale)
+    assert e.value.status == -6
+    torch.cuda.synchronize()
+    assert torch.equal(bits(t["k_cache"].cpu()), bits(kc1.cpu()))
+    assert torch.equal(bits(t["v_cache"].cpu()), bits(vc1.cpu()))
+    del kc0, vc0
+
+    sp = workloads.make_workload(2, seed=96, device="cuda", seq_lens=[100, 70, 90],
+                                 shared_prefix_tokens=64)
+    ts = sp.tensors
+    sbt = sp.block_tables_tensor("cuda")
+    slens = sp.seq_lens_tensor("cuda")
+    sargs = (ts["query"], ts["key"], ts["value"], ts["k_cache"], ts["v_cache"])
+    binding.decode_shared_prefix_append(*sargs, sbt, slens, sp.max_seq_len, sp.scale, 4)  # valid
+    at_prefix = slens.clone()
+    at_prefix[1] = 64  # the new token would be position 63, inside the shared blocks
+    with pytest.raises(binding.PAError) as e:
+        binding.decode_shared_prefix_append(*sargs, sbt, at_prefix, sp.max_seq_len, sp.scale, 4)
+    assert e.value.status == -6
+    torch.cuda.synchronize()
