@@ -40,6 +40,38 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(binding.SIGNATURES)
 
 
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++11")])
+def test_headers_build_a_c_and_cxx_caller(lib, tmp_path, compiler, std):
+    """Both headers compile as strict C99 and C++11, every declared function
+    links against libpa.so by its declared name, and host-only calls run."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    names = _declared()
+    src = tmp_path / ("caller.c" if compiler == "gcc" else "caller.cpp")
+    src.write_text(
+        '#include <stdio.h>\n#include "pa.h"\n#include "pa_sched.h"\n'
+        "typedef void (*fn)(void);\n"
+        "static fn table[] = {\n"
+        + "".join(f"  (fn)&{n},\n" for n in names)
+        + "};\n"
+        "int main(void) {\n"
+        "  unsigned n = 0, i;\n"
+        "  for (i = 0; i < sizeof table / sizeof table[0]; ++i) n += table[i] != 0;\n"
+        '  printf("%u %d %s\\n", n, pa_version(), pa_status_string(0));\n'
+        "  return 0;\n}\n")
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(binding.LIB_PATH)
+    subprocess.run([compiler, std, "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-Wno-cast-function-type", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe), "-L", libdir, "-lpa", f"-Wl,-rpath,{libdir}"],
+                   check=True, capture_output=True, text=True)
+    got = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert got[:2] == [str(len(names)), "100"], got
+    assert got[2].startswith(binding.STATUS[0]), got
+
+
 def test_status_strings_and_version(lib):
     for code, name in binding.STATUS.items():
         assert binding.status_string(code).startswith(name)
